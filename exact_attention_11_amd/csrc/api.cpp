@@ -1,0 +1,220 @@
+// C ABI of libfattn: argument validation and kernel dispatch.
+//
+// Every check happens on the host before anything is launched; an invalid call
+// returns a status and leaves a message in a thread-local buffer.  No
+// exception crosses the ABI and no device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fattn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Shared shape checks of the dense forward calls.
+int check_dense(const char* fn, const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                int H, int Hkv, int N, float scale, int causal) {
+  if (B < 0 || N < 0) return fail(FATTN_ERR_INVALID_ARG, "%s: B and N must be >= 0 (got B=%d N=%d)", fn, B, N);
+  if (H < 1 || Hkv < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: H and Hkv must be >= 1 (got H=%d Hkv=%d)", fn, H, Hkv);
+  if (H % Hkv != 0) return fail(FATTN_ERR_INVALID_ARG, "%s: H=%d is not a multiple of Hkv=%d", fn, H, Hkv);
+  if (causal != 0 && causal != 1) return fail(FATTN_ERR_INVALID_ARG, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: scale must be finite and >= 0 (got %g)", fn, (double)scale);
+  if (B == 0 || N == 0) return FATTN_OK;
+  if (!q || !k || !v || !o) return fail(FATTN_ERR_INVALID_ARG, "%s: q, k, v and o must be non-null", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  const double rows = (double)B * H * N;
+  if (rows > 2147483647.0) return fail(FATTN_ERR_INVALID_ARG, "%s: B*H*N too large", fn);
+  return FATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fattn_status_string(int status) {
+  switch (status) {
+    case FATTN_OK: return "FATTN_OK";
+    case FATTN_ERR_INVALID_ARG: return "FATTN_ERR_INVALID_ARG";
+    case FATTN_ERR_UNSUPPORTED: return "FATTN_ERR_UNSUPPORTED";
+    case FATTN_ERR_HIP: return "FATTN_ERR_HIP";
+    case FATTN_ERR_INTERNAL: return "FATTN_ERR_INTERNAL";
+    default: return "FATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* fattn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+             float scale, int causal, void* stream) {
+  int st = check_dense("attn_fwd", q, k, v, o, lse, B, H, Hkv, N, scale, causal);
+  if (st != FATTN_OK) return st;
+  if (d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "attn_fwd: d=%d not supported (64 or 128)", d);
+  if (B == 0 || N == 0) return ok();
+  fattn::TileArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.offsets = nullptr;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.c = scale * kLog2e;
+  a.inv_n = 1.f;
+  a.causal = causal;
+  a.epi = fattn::Epilogue::Softmax;
+  return hip_status(fattn::launch_tile_bf16(a, static_cast<hipStream_t>(stream)), "attn_fwd launch");
+}
+
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+                 float scale, int causal, void* stream) {
+  int st = check_dense("attn_fwd_f32", q, k, v, o, lse, B, H, Hkv, N, scale, causal);
+  if (st != FATTN_OK) return st;
+  if (d != 64) return fail(FATTN_ERR_UNSUPPORTED, "attn_fwd_f32: d=%d not supported (64)", d);
+  if (B == 0 || N == 0) return ok();
+  fattn::F32Args a{};
+  a.q = static_cast<const float*>(q);
+  a.k = static_cast<const float*>(k);
+  a.v = static_cast<const float*>(v);
+  a.o = static_cast<float*>(o);
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.c = scale * kLog2e;
+  a.causal = causal;
+  return hip_status(fattn::launch_prefill_f32(a, static_cast<hipStream_t>(stream)), "attn_fwd_f32 launch");
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits) {
+  if (B < 0 || H < 1 || Hkv < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;
+  int s = num_splits;
+  if (s == 0) {
+    if (lmax_hint < 1) return 0;
+    s = fattn::decode_auto_splits(B, Hkv, lmax_hint);
+  }
+  const size_t bytes = (size_t)B * H * s * ((size_t)d + 1) * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k, void* o,
+                float* lse, int B, int H, int Hkv, int Lmax, int d, float scale, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const char* fn = "attn_decode";
+  if (B < 0) return fail(FATTN_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+  if (H < 1 || Hkv < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: H and Hkv must be >= 1", fn);
+  if (H % Hkv != 0) return fail(FATTN_ERR_INVALID_ARG, "%s: H=%d is not a multiple of Hkv=%d", fn, H, Hkv);
+  if (Lmax < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: Lmax must be >= 1 (got %d)", fn, Lmax);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: scale must be finite and >= 0 (got %g)", fn, (double)scale);
+  if (num_splits < 0 || num_splits > 64)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: num_splits must be 0 (auto) or 1..64 (got %d)", fn, num_splits);
+  const int G = H / Hkv;
+  if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4 or 8)", fn, G);
+  if (B == 0) return ok();
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !workspace)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: q, caches, seqlens_k, o and workspace must be non-null", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace) ||
+      (lse && !aligned16(lse)))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if ((double)B * Hkv * Lmax * d > 9.0e15) return fail(FATTN_ERR_INVALID_ARG, "%s: cache too large", fn);
+  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax) : num_splits;
+  const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
+  if (workspace_bytes < need)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                workspace_bytes, need);
+  fattn::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Lmax = Lmax;
+  a.d = d;
+  a.c = scale * kLog2e;
+  a.splits = splits;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)B * H * splits * d;
+  return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o, const int32_t* offsets, int B, int H,
+                     int d, int max_seqlen, float alpha, float inv_n, int causal, void* stream) {
+  const char* fn = "attn_hstu_jagged";
+  if (B < 0 || max_seqlen < 0)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: B and max_seqlen must be >= 0 (got B=%d max_seqlen=%d)", fn, B,
+                max_seqlen);
+  if (H < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: H must be >= 1", fn);
+  if (causal != 0 && causal != 1) return fail(FATTN_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  if (!std::isfinite(alpha) || !std::isfinite(inv_n))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: alpha and inv_n must be finite", fn);
+  if (d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (64 or 128)", fn, d);
+  if (B == 0 || max_seqlen == 0) return ok();
+  if (!q || !k || !v || !o || !offsets)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: q, k, v, o and offsets must be non-null", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  fattn::TileArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = nullptr;
+  a.offsets = offsets;
+  a.B = B;
+  a.H = H;
+  a.Hkv = H;
+  a.N = max_seqlen;
+  a.d = d;
+  a.c = alpha;
+  a.inv_n = inv_n;
+  a.causal = causal;
+  a.epi = fattn::Epilogue::Silu;
+  return hip_status(fattn::launch_tile_bf16(a, static_cast<hipStream_t>(stream)), "attn_hstu_jagged launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal kernel launchers of libfattn (host side).  The C ABI in api.cpp
+// validates arguments and then calls exactly one of these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fattn {
+
+// Pointwise step applied to each score of the fused tile loop.
+enum class Epilogue : int {
+  Softmax = 0,  // online softmax: running max, running sum, rescale
+  Silu = 1,     // HSTU: silu(alpha * s), no normalisation
+};
+
+struct TileArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // softmax only; may be null
+  const int32_t* offsets;  // jagged layout only (null for dense)
+  int B, H, Hkv;
+  int N;                   // dense: sequence length; jagged: max_seqlen
+  int d;
+  float c;                 // softmax: scale * log2(e); silu: alpha
+  float inv_n;             // silu: 1/n
+  int causal;
+  Epilogue epi;
+};
+
+// bf16 MFMA tile kernel (dense softmax prefill or jagged SiLU).
+hipError_t launch_tile_bf16(const TileArgs& a, hipStream_t stream);
+
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int B, H, Hkv, N, d;
+  float c;  // scale * log2(e)
+  int causal;
+};
+
+hipError_t launch_prefill_f32(const F32Args& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Lmax, d;
+  float c;  // scale * log2(e)
+  int splits;
+  float* part_o;    // [B, H, splits, d]
+  float* part_lse;  // [B, H, splits]
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Automatic split count for a decode shape.
+int decode_auto_splits(int B, int Hkv, int Lmax);
+
+}  // namespace fattn

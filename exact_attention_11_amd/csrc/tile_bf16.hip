@@ -1,0 +1,383 @@
+// Fused, tiled exact attention on gfx950 matrix cores (bf16 in, fp32 accumulate).
+//
+// One workgroup of four 64-wide waves owns 128 query rows of one (batch, head);
+// each wave owns 32 of them.  K and V tiles stream from HBM through LDS (double
+// buffered, one barrier per tile) while the score tile and the output
+// accumulator stay in registers, so the N x N score matrix never reaches HBM
+// (CANN ops-transformer FlashAttention page: tiles sized to the matrix unit,
+// block results kept on chip, only the final output written back).
+//
+// Per tile the wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on
+// the M side, queries on the N side).  The accumulator then holds, in each lane,
+// 16 scores of ONE query column, which is (a) the layout of the B operand of the
+// next product O^T += V^T P^T, so P never leaves registers, and (b) makes the
+// row max and row sum mostly in-lane: only lanes l and l^32 share a query.
+//
+// Keys are fed to the first product in a permuted row order (bits 2 and 3 of the
+// in-block key index swapped) so that each lane's 8 P values for one K=16 step
+// of the second product are 8 CONSECUTIVE keys; V^T can then be read from LDS
+// with one 16-byte load per step.  V is transposed while it is written into LDS
+// (register byte-permutes), with a row-dependent XOR swizzle of 16-byte chunks
+// so that the 16-byte reads are bank-conflict free.
+//
+// Two pointwise epilogues share the loop:
+//  * Softmax: online softmax with a running row max m and running sum l
+//    (CANN ops-transformer FlashAttention page, steps 1-4; FlashAttention (TH)
+//    page, online softmax).  Scores are handled in base 2 with scale*log2(e)
+//    folded into one FMA.  The output is rescaled only when some row's tile max
+//    exceeds the reference max by more than 2^8 -- between rescales every
+//    exponent is relative to a common reference that is at most 8 below the
+//    true running max, so weights stay <= 256 and the final O/l and LSE are
+//    the same quantities.
+//  * Silu: HSTU pointwise attention, silu(alpha s) with no normalisation
+//    (HSTU page, the listing and optimisation one).
+//
+// Causal masking is generated in the kernel from tile positions: tiles wholly
+// below the diagonal run unmasked, tiles straddling it are masked per element,
+// tiles wholly above it are never loaded or computed (HSTU page, optimisation
+// two).  Rows and keys past the sequence end (ragged N, jagged sequences) are
+// masked the same way and their loads are predicated off.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;              // query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+template <int D>
+struct Cfg;
+template <>
+struct Cfg<128> {
+  static constexpr int BN = 64;
+};
+template <>
+struct Cfg<64> {
+  static constexpr int BN = 128;
+};
+
+template <int D, int BN>
+struct Lds {
+  static constexpr int kRow = (D + 8) * 2;  // K row: D bf16 + 16-byte pad
+  static constexpr int kBytes = BN * kRow;
+  static constexpr int vRow = BN * 2;       // V^T row: BN bf16, swizzled
+  static constexpr int vBytes = D * vRow;
+  static constexpr int stage = kBytes + vBytes;
+  static constexpr int total = 2 * stage;
+  // XOR applied to the 16-byte chunk index of V^T row m: rows that share a
+  // 256-byte bank line get different chunk orders.
+  __device__ static __forceinline__ int vswz(int m) {
+    return BN == 64 ? ((m >> 1) & 7) : (m & 15);
+  }
+};
+
+// In-block key order of the first product: swap bits 2 and 3.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (relative to the 32-key block) held by accumulator element e = 4j + r of
+// a lane in half g2 (lane / 32).
+__device__ __forceinline__ int acc_key(int e, int g2) {
+  const int j = e >> 2, r = e & 3;
+  return 16 * (j >> 1) + 8 * g2 + 4 * (j & 1) + r;
+}
+
+template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
+__global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int NKB = BN / 32;  // 32-key blocks per tile
+  constexpr int NDB = D / 32;   // 32-row blocks of d
+  constexpr int NDC = D / 16;   // K=16 steps over d
+  using L = Lds<D, BN>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n32 = lane & 31;
+  const int g2 = lane >> 5;
+
+  // ---- work item: (batch, head, query block), heaviest blocks first, all
+  // blocks of a head on one XCD (dispatch is round-robin over 8 XCDs).
+  const int G = gridDim.x;
+  int wid = blockIdx.x;
+  if ((G & 7) == 0) wid = (wid & 7) * (G >> 3) + (wid >> 3);
+  const int qb = nq - 1 - (wid % nq);
+  const int bh = wid / nq;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+
+  const uint16_t* qp;
+  const uint16_t* kp;
+  const uint16_t* vp;
+  uint16_t* op;
+  long row_stride;  // elements between consecutive rows
+  int len;
+  long lse_base = 0;
+  if constexpr (JAGGED) {
+    const int s0 = a.offsets[b];
+    const int s1 = a.offsets[b + 1];
+    len = min(s1 - s0, a.N);
+    row_stride = (long)a.H * D;
+    const long base = ((long)s0 * a.H + h) * D;
+    qp = (const uint16_t*)a.q + base;
+    kp = (const uint16_t*)a.k + base;
+    vp = (const uint16_t*)a.v + base;
+    op = (uint16_t*)a.o + base;
+  } else {
+    len = a.N;
+    row_stride = D;
+    const int g = h / (a.H / a.Hkv);
+    const long qbase = ((long)b * a.H + h) * a.N * D;
+    const long kbase = ((long)b * a.Hkv + g) * a.N * D;
+    qp = (const uint16_t*)a.q + qbase;
+    op = (uint16_t*)a.o + qbase;
+    kp = (const uint16_t*)a.k + kbase;
+    vp = (const uint16_t*)a.v + kbase;
+    lse_base = ((long)b * a.H + h) * a.N;
+  }
+  const int q0 = qb * kBM;
+  if (len <= 0 || q0 >= len) return;  // uniform over the workgroup
+
+  const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  const int q0w = q0 + 32 * wv;
+  const bool wave_live = q0w < len;
+  const int qrow = q0w + n32;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.
+  bf16x8 qf[NDC];
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (qrow < len) t = ldg16(qp + (long)qrow * row_stride + 16 * c + 8 * g2);
+    qf[c] = as_bf16x8(t);
+  }
+
+  // ---- global -> register staging of one K/V tile
+  constexpr int KCH = D / 8;                     // 16-byte chunks per K row
+  constexpr int KLOADS = BN * KCH / kThreads;    // 4
+  const int vkg = tid % (BN / 4);                // V: 4 keys x 8 d per thread
+  const int vdg = tid / (BN / 4);
+  u32x4 kr[KLOADS], vr[4];
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int ci = tid + kThreads * i;
+      const int row = k0 + ci / KCH;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (row < len) t = ldg16(kp + (long)row * row_stride + (ci % KCH) * 8);
+      kr[i] = t;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = k0 + 4 * vkg + i;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (row < len) t = ldg16(vp + (long)row * row_stride + vdg * 8);
+      vr[i] = t;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* sk = smem + buf * L::stage;
+    unsigned char* sv = sk + L::kBytes;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int ci = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(sk + (ci / KCH) * L::kRow + (ci % KCH) * 16) = kr[i];
+    }
+    const int chunk = vkg >> 1;
+    const int half = vkg & 1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 8 * vdg + e;
+      const int w = e >> 1;
+      u32x2 t;
+      if (e & 1) {
+        t[0] = pair_hi(vr[0][w], vr[1][w]);
+        t[1] = pair_hi(vr[2][w], vr[3][w]);
+      } else {
+        t[0] = pair_lo(vr[0][w], vr[1][w]);
+        t[1] = pair_lo(vr[2][w], vr[3][w]);
+      }
+      *reinterpret_cast<u32x2*>(sv + m * L::vRow + ((chunk ^ L::vswz(m)) << 4) + (half << 3)) = t;
+    }
+  };
+
+  // ---- accumulators and running statistics
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  float m_ref = kNegInf;  // base-2 reference max (scaled)
+  float l_part = 0.f;     // this lane's share of the row sum
+  const float cexp = a.c;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    const int k0 = j * BN;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) load_tile(k0 + BN);
+
+    const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
+    if (active) {
+      const unsigned char* sk = smem + buf * L::stage;
+      const unsigned char* sv = sk + L::kBytes;
+      // S^T = K Q^T
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(
+              sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], s[kb], 0, 0, 0);
+        }
+      }
+
+      const bool masked = (CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len);
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * kb + acc_key(e, g2);
+            const bool vis = (key < len) && (!CAUSAL || key <= qrow);
+            if (!vis) s[kb][e] = kNegInf;
+          }
+      }
+
+      uint32_t pk[NKB][8];  // bf16 pairs of P (or of silu scores)
+      if constexpr (EPI == Epilogue::Softmax) {
+        float mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+        mt = fmaxf(mt, xor32(mt));
+        const float mts = (mt == kNegInf) ? kNegInf : mt * cexp;
+        if (wave_any(mts > m_ref + kRescaleSlack)) {
+          const float mn = fmaxf(m_ref, mts);
+          const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m_ref - mn);
+          m_ref = mn;
+          l_part *= alpha;
+#pragma unroll
+          for (int i = 0; i < NDB; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][e] *= alpha;
+        }
+        const float nm = -m_ref;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            p[e] = exp2_hw(__builtin_fmaf(s[kb][e], cexp, nm));
+            if (masked) p[e] = (s[kb][e] == kNegInf) ? 0.f : p[e];
+            l_part += p[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        }
+      } else {
+        const float alpha = cexp;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float y[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float x = s[kb][e] * alpha;
+            y[e] = x * rcp_hw(1.f + exp2_hw(-x * kLog2e));
+            if (masked) y[e] = (s[kb][e] == kNegInf) ? 0.f : y[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+        }
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
+          const bf16x8 pb = as_bf16x8(pw);
+          const int chunk = 4 * kb + 2 * jj + g2;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int m = 32 * db + n32;
+            const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + m * L::vRow + ((chunk ^ L::vswz(m)) << 4));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_live || qrow >= len) return;
+
+  float scale_out;
+  if constexpr (EPI == Epilogue::Softmax) {
+    const float lt = l_part + xor32(l_part);
+    scale_out = lt > 0.f ? 1.f / lt : 0.f;
+    if (a.lse != nullptr && g2 == 0) {
+      a.lse[lse_base + qrow] = lt > 0.f ? (m_ref + log2_hw(lt)) * kLn2 : kNegInf;
+    }
+  } else {
+    scale_out = a.inv_n;
+  }
+  uint16_t* orow = op + (long)qrow * row_stride;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      u32x2 t;
+      t[0] = pack_bf16x2(acc[db][4 * jq] * scale_out, acc[db][4 * jq + 1] * scale_out);
+      t[1] = pack_bf16x2(acc[db][4 * jq + 2] * scale_out, acc[db][4 * jq + 3] * scale_out);
+      stg8(orow + 32 * db + 8 * jq + 4 * g2, t);
+    }
+}
+
+template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
+hipError_t launch_one(const TileArgs& a, hipStream_t stream) {
+  const int nq = (a.N + kBM - 1) / kBM;
+  const long grid = (long)nq * a.H * a.B;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((tile_kernel<D, CAUSAL, EPI, JAGGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nq);
+  return hipGetLastError();
+}
+
+template <int D, Epilogue EPI, bool JAGGED>
+hipError_t launch_causal(const TileArgs& a, hipStream_t s) {
+  return a.causal ? launch_one<D, true, EPI, JAGGED>(a, s) : launch_one<D, false, EPI, JAGGED>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_tile_bf16(const TileArgs& a, hipStream_t stream) {
+  if (a.epi == Epilogue::Softmax) {
+    if (a.d == 128) return launch_causal<128, Epilogue::Softmax, false>(a, stream);
+    if (a.d == 64) return launch_causal<64, Epilogue::Softmax, false>(a, stream);
+  } else {
+    if (a.d == 128) return launch_causal<128, Epilogue::Silu, true>(a, stream);
+    if (a.d == 64) return launch_causal<64, Epilogue::Silu, true>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fattn

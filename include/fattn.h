@@ -1,0 +1,148 @@
+/*
+ * libfattn -- exact attention for AMD MI355X (gfx950), C ABI.
+ *
+ * Every entry point is asynchronous on the HIP stream it is given
+ * (hipStream_t passed as void*; NULL means the default stream).  All tensor
+ * pointers are DEVICE pointers owned by the caller; the library never
+ * allocates, frees or retains device memory and keeps no state between calls
+ * apart from a thread-local error string.  Calls are re-entrant and may run
+ * on concurrent streams.
+ *
+ * Arguments are validated on the host before anything is launched; an
+ * invalid call launches nothing and returns a non-zero status.  Values that
+ * live in device memory (sequence lengths, offsets) are not read by the host:
+ * kernels clamp them to the sizes passed in, so a violated precondition gives
+ * unspecified output but no out-of-bounds access.  Kernel faults surface at
+ * the caller's next synchronisation.
+ *
+ * Element types: "bf16" is IEEE-style bfloat16 stored as uint16; "f32" is
+ * IEEE binary32.  Every tensor is dense and contiguous in the layout given,
+ * and every tensor pointer must be 16-byte aligned.
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FATTN_OK 0
+#define FATTN_ERR_INVALID_ARG 1 /* argument out of its documented range        */
+#define FATTN_ERR_UNSUPPORTED 2 /* valid, but no kernel for it (e.g. d = 96)   */
+#define FATTN_ERR_HIP 3         /* HIP reported an error at launch             */
+#define FATTN_ERR_INTERNAL 4
+
+/*
+ * attn_fwd -- fused exact attention, bf16 in / bf16 out, fp32 accumulation.
+ *
+ *   O = softmax(scale * Q K^T [+ causal mask]) V,   LSE = m + ln(sum exp(s - m))
+ *
+ * The operation is the standard attention formula (FlashAttention (TH) page,
+ * the section on standard attention; ledger page, "FLOPs" section), computed
+ * as one tiled kernel with an online softmax (CANN ops-transformer
+ * FlashAttention page, steps 1-4 of the solution) so that the N x N score
+ * matrix never reaches device memory.  The causal mask is generated in the
+ * kernel and tiles above the diagonal are skipped (HSTU page, optimisation
+ * two, in-kernel mask).
+ *
+ *   q    bf16 [B, H,   N, d]
+ *   k, v bf16 [B, Hkv, N, d]   query head h reads key/value head h / (H/Hkv)
+ *   o    bf16 [B, H,   N, d]   written
+ *   lse  f32  [B, H,   N]      written (natural log), or NULL to skip
+ *   H % Hkv == 0; d in {64, 128}; scale finite and >= 0;
+ *   causal in {0, 1}: 1 lets row i see keys j <= i.
+ *   B == 0 or N == 0 is a valid empty call (nothing launched).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             void* stream);
+
+/*
+ * attn_fwd_f32 -- the same operation with f32 q, k, v, o (same layouts), f32
+ * arithmetic throughout (probabilities are not rounded).  d == 64 only.
+ */
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 void* stream);
+
+/*
+ * attn_decode_workspace_bytes -- device workspace attn_decode needs for this
+ * shape: room for one partial output row (f32, d values) and one partial
+ * log-sum-exp (f32) per (b, h, split), rounded up to 256 bytes.
+ * num_splits == 0 asks for the automatic choice attn_decode would make for
+ * the given Lmax (pass it as lmax_hint; ignored otherwise).  Returns 0 for an
+ * invalid shape.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits);
+
+/*
+ * attn_decode -- one new query token per sequence against a KV cache,
+ * split over the key length, then merged by log-sum-exp weights.
+ *
+ * Decode is the bandwidth-bound step the ledger page describes (bandwidth
+ * section: s_j = q^T k_j over all history keys, o = sum_j p_j v_j, O(n d)
+ * bytes per step), and prefill and decode take different kernels (CANN
+ * ops-transformer FlashAttention page, prefill vs decode).  Kernel 1 gives
+ * each (sequence, kv-head, split) a contiguous chunk of keys and writes a
+ * normalised partial output and its log-sum-exp to the workspace; kernel 2
+ * combines the partials of each (sequence, head).
+ *
+ *   q          bf16 [B, H, d]            (one token per sequence)
+ *   k_cache    bf16 [B, Hkv, Lmax, d]
+ *   v_cache    bf16 [B, Hkv, Lmax, d]
+ *   seqlens_k  int32 [B], device memory; the query attends to cache rows
+ *              [0, seqlens_k[b]); rows at or beyond it are never read.
+ *              Values are clamped to [0, Lmax]; a sequence of length 0 gives
+ *              O = 0 and LSE = -inf.
+ *   o          bf16 [B, H, d]            written
+ *   lse        f32  [B, H]               written, or NULL
+ *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8}; d == 128; scale finite, >= 0.
+ *   num_splits 0 = automatic, else 1..64.
+ *   workspace  device buffer of at least attn_decode_workspace_bytes(...)
+ *              bytes for the same arguments; contents on entry are ignored.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens_k, void* o, float* lse,
+                int B, int H, int Hkv, int Lmax, int d, float scale,
+                int num_splits, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * attn_hstu_jagged -- HSTU pointwise attention over packed variable-length
+ * sequences (no padding).
+ *
+ * Per sequence b and head h, following the order of the HSTU page's listing
+ * (x = Q K^T; x *= alpha; x = silu(x); x *= mask / n; O = x V) with the mask
+ * generated in the kernel (optimisation two) and the sequences packed by
+ * offsets (optimisation three, jagged tensors):
+ *
+ *   O[t] = inv_n * sum_{j visible from t} silu(alpha * q_t . k_j) v_j
+ *
+ * with silu(x) = x / (1 + e^-x); there is no softmax and no LSE.
+ *
+ *   q, k, v   bf16 [T, H, d] packed: sequence b owns rows
+ *             [offsets[b], offsets[b+1])
+ *   o         bf16 [T, H, d]  written (rows of every sequence)
+ *   offsets   int32 [B + 1], device memory, non-decreasing, offsets[0] = 0
+ *   max_seqlen >= every sequence length (rows beyond it are not computed)
+ *   d in {64, 128}; alpha, inv_n finite; causal in {0, 1} (1: key j <= row i).
+ */
+int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o,
+                     const int32_t* offsets, int B, int H, int d, int max_seqlen,
+                     float alpha, float inv_n, int causal, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fattn_status_string(int status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* fattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

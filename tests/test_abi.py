@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every function include/fattn.h declares, and rejects invalid arguments before
+launching anything (no call here reaches the GPU)."""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_attention_11_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fattn.h")
+
+# Fake, 16-byte aligned, never dereferenced: validation fails before any use.
+P = 0x10000
+S0 = 0  # default stream handle; never used by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED_SYMBOLS), names
+    lib = fa.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+
+
+def test_status_strings():
+    assert fa.fattn_status_string(0) == "FATTN_OK"
+    assert fa.fattn_status_string(1) == "FATTN_ERR_INVALID_ARG"
+    assert fa.fattn_status_string(2) == "FATTN_ERR_UNSUPPORTED"
+    assert fa.fattn_status_string(3) == "FATTN_ERR_HIP"
+    assert fa.fattn_status_string(99) == "FATTN_ERR_UNKNOWN"
+
+
+def _fwd(fn, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=4, Hkv=2, N=16, d=128, scale=0.1, causal=1)
+    args.update(kw)
+    fn(stream=S0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(o=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(q=P + 8), fa.FATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 4), fa.FATTN_ERR_INVALID_ARG),
+    (dict(H=3), fa.FATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FATTN_ERR_INVALID_ARG),
+    (dict(N=-5), fa.FATTN_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FATTN_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FATTN_ERR_INVALID_ARG),
+    (dict(d=96), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FATTN_ERR_UNSUPPORTED),
+])
+def test_attn_fwd_rejects(kw, status):
+    with pytest.raises(fa.FattnError) as e:
+        _fwd(fa.attn_fwd, **kw)
+    assert e.value.status == status
+    assert fa.fattn_last_error().startswith("attn_fwd")
+
+
+def test_attn_fwd_f32_rejects_d128():
+    with pytest.raises(fa.FattnError) as e:
+        _fwd(fa.attn_fwd_f32, d=128)
+    assert e.value.status == fa.FATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", [fa.attn_fwd, fa.attn_fwd_f32])
+def test_empty_calls_launch_nothing(fn):
+    d = 64
+    _fwd(fn, q=0, k=0, v=0, o=0, B=0, d=d)
+    _fwd(fn, q=0, k=0, v=0, o=0, N=0, d=d)
+
+
+def _dec(**kw):
+    B, H, Hkv, L, d = 2, 8, 2, 100, 128
+    ws = fa.attn_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+    args = dict(q=P, k_cache=P, v_cache=P, seqlens_k=P, o=P, lse=None, B=B, H=H, Hkv=Hkv, Lmax=L, d=d, scale=0.1,
+                num_splits=0, workspace=P, workspace_bytes=ws)
+    args.update(kw)
+    fa.attn_decode(stream=S0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(seqlens_k=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(workspace_bytes=16), fa.FATTN_ERR_INVALID_ARG),
+    (dict(num_splits=65), fa.FATTN_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FATTN_ERR_INVALID_ARG),
+    (dict(Lmax=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(H=7), fa.FATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(d=64), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(H=6, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(H=32, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
+])
+def test_attn_decode_rejects(kw, status):
+    with pytest.raises(fa.FattnError) as e:
+        _dec(**kw)
+    assert e.value.status == status
+
+
+def test_decode_workspace_size():
+    # one f32 row of d plus one f32 LSE per (b, h, split), rounded to 256 B
+    assert fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 64) == 16 * 32 * 64 * 129 * 4
+    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 1) == 768
+    # automatic split count for Lmax = 1 is one split: 4128 bytes -> 4352
+    assert fa.attn_decode_workspace_bytes(2, 4, 2, 1, 128, 0) == 4352
+    auto = fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 0)
+    assert auto > 0 and auto % 256 == 0
+    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 65) == 0
+    assert fa.attn_decode_workspace_bytes(1, 0, 1, 10, 128, 1) == 0
+
+
+def _hstu(**kw):
+    args = dict(q=P, k=P, v=P, o=P, offsets=P, B=2, H=4, d=64, max_seqlen=100, alpha=0.125, inv_n=1 / 4096, causal=1)
+    args.update(kw)
+    fa.attn_hstu_jagged(stream=S0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(offsets=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(q=P + 2), fa.FATTN_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FATTN_ERR_INVALID_ARG),
+    (dict(max_seqlen=-1), fa.FATTN_ERR_INVALID_ARG),
+    (dict(H=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FATTN_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), fa.FATTN_ERR_INVALID_ARG),
+    (dict(d=32), fa.FATTN_ERR_UNSUPPORTED),
+])
+def test_attn_hstu_rejects(kw, status):
+    with pytest.raises(fa.FattnError) as e:
+        _hstu(**kw)
+    assert e.value.status == status
+
+
+def test_hstu_empty_calls_launch_nothing():
+    _hstu(q=0, k=0, v=0, o=0, offsets=0, B=0)
+    _hstu(q=0, k=0, v=0, o=0, offsets=0, max_seqlen=0)
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "libfattn.so"))
+    with pytest.raises(fa.FattnLibraryError):
+        fa.library()

@@ -1,0 +1,306 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element and span several tiles with ragged
+tails; the full-size workloads compare sampled rows that the oracle computes
+one by one (same launch configuration as the benchmark).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import exact_attention_11_amd as fa
+import oracle
+from synthgen import TENSOR_K, TENSOR_Q, TENSOR_V, bf16_bits_to_f64, normal_bf16, normal_f32
+from synthgen import workloads as W
+
+from _util import (assert_bf16, assert_lse, bf16_dev_to_f64, f32_ok, lse_ok, sample_rows, to_dev,
+                    to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_fwd(q_bits, k_bits, v_bits, B, H, Hkv, N, d, scale, causal, want_lse=True):
+    q, k, v = to_dev_bf16(q_bits), to_dev_bf16(k_bits), to_dev_bf16(v_bits)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda") if want_lse else None
+    fa.attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# --- f32 path ------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_f32_workload(causal):
+    _need_gpu()
+    c = W.TINY_F32
+    x = W.dense_inputs(c)
+    O_ref, L_ref = oracle.attention_forward(x.f64("q"), x.f64("k"), x.f64("v"), c.scale, causal)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((c.B, c.H, c.N), dtype=torch.float32, device="cuda")
+    fa.attn_fwd_f32(q, k, v, o, lse, c.B, c.H, c.Hkv, c.N, c.d, c.scale, int(causal))
+    torch.cuda.synchronize()
+    ok, r = f32_ok(o.cpu().numpy(), O_ref)
+    assert ok, str(r)
+    ok, r = lse_ok(lse.cpu().numpy(), L_ref)
+    assert ok and r.max_abs <= 1e-5, str(r)
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 200])
+def test_f32_ragged_and_gqa(N):
+    _need_gpu()
+    B, H, Hkv, d, scale = 2, 4, 2, 64, 0.125
+    q = normal_f32(7, TENSOR_Q, (B, H, N, d))
+    k = normal_f32(7, TENSOR_K, (B, Hkv, N, d))
+    v = normal_f32(7, TENSOR_V, (B, Hkv, N, d))
+    for causal in (0, 1):
+        O_ref, L_ref = oracle.attention_forward(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                                scale, bool(causal))
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.attn_fwd_f32(to_dev(q), to_dev(k), to_dev(v), o, lse, B, H, Hkv, N, d, scale, causal)
+        torch.cuda.synchronize()
+        ok, r = f32_ok(o.cpu().numpy(), O_ref)
+        assert ok, f"causal={causal}: {r}"
+        assert lse_ok(lse.cpu().numpy(), L_ref)[0]
+
+
+# --- bf16 prefill, small shapes (every element) -------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 64, 129, 255, 300])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bf16_small_every_element(d, N, causal):
+    _need_gpu()
+    B, H, Hkv = 2, 4, 2
+    scale = 1.0 / math.sqrt(d)
+    seed = 100 + N + d
+    q = normal_bf16(seed, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(seed, TENSOR_K, (B, Hkv, N, d))
+    v = normal_bf16(seed, TENSOR_V, (B, Hkv, N, d))
+    o, lse = run_fwd(q, k, v, B, H, Hkv, N, d, scale, causal)
+    O_ref, L_ref = oracle.attention_forward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), scale,
+                                            bool(causal))
+    assert_bf16(bf16_dev_to_f64(o), O_ref, f"N={N} d={d} causal={causal}")
+    assert_lse(lse.cpu().numpy(), L_ref, f"N={N} d={d} causal={causal}")
+
+
+def test_bf16_causal_row_zero_is_exactly_v0():
+    _need_gpu()
+    B, H, N, d = 1, 3, 200, 128
+    q = normal_bf16(5, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(5, TENSOR_K, (B, H, N, d))
+    v = normal_bf16(5, TENSOR_V, (B, H, N, d))
+    o, lse = run_fwd(q, k, v, B, H, H, N, d, 0.1, 1)
+    got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[:, :, 0], v[:, :, 0])
+    s00 = 0.1 * np.einsum("bhd,bhd->bh", bf16_bits_to_f64(q[:, :, 0]), bf16_bits_to_f64(k[:, :, 0]))
+    assert np.max(np.abs(lse.cpu().numpy()[:, :, 0] - s00)) < 1e-5
+
+
+def test_bf16_zero_scale_is_running_mean():
+    _need_gpu()
+    B, H, N, d = 1, 2, 150, 64
+    q = normal_bf16(6, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(6, TENSOR_K, (B, H, N, d))
+    v = normal_bf16(6, TENSOR_V, (B, H, N, d))
+    for causal in (0, 1):
+        o, lse = run_fwd(q, k, v, B, H, H, N, d, 0.0, causal)
+        O_ref, L_ref = oracle.attention_forward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), 0.0,
+                                                bool(causal))
+        assert_bf16(bf16_dev_to_f64(o), O_ref, f"scale=0 causal={causal}")
+        assert_lse(lse.cpu().numpy(), L_ref)
+
+
+def test_bf16_deterministic_and_lse_optional():
+    _need_gpu()
+    B, H, N, d = 1, 4, 333, 128
+    q = normal_bf16(8, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(8, TENSOR_K, (B, H, N, d))
+    v = normal_bf16(8, TENSOR_V, (B, H, N, d))
+    o1, l1 = run_fwd(q, k, v, B, H, H, N, d, 0.09, 1)
+    o2, l2 = run_fwd(q, k, v, B, H, H, N, d, 0.09, 1)
+    o3, _ = run_fwd(q, k, v, B, H, H, N, d, 0.09, 1, want_lse=False)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_bf16_large_score_offset_no_overflow():
+    """Scores around +-100 (far beyond exp range without the max shift)."""
+    _need_gpu()
+    B, H, N, d = 1, 2, 257, 128
+    q = normal_bf16(9, TENSOR_Q, (B, H, N, d), 4.0)
+    k = normal_bf16(9, TENSOR_K, (B, H, N, d), 4.0)
+    v = normal_bf16(9, TENSOR_V, (B, H, N, d))
+    for causal in (0, 1):
+        o, lse = run_fwd(q, k, v, B, H, H, N, d, 1.0 / math.sqrt(d), causal)
+        O_ref, L_ref = oracle.attention_forward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v),
+                                                1.0 / math.sqrt(d), bool(causal))
+        assert_bf16(bf16_dev_to_f64(o), O_ref, f"offset causal={causal}")
+        assert_lse(lse.cpu().numpy(), L_ref)
+
+
+# --- bf16 prefill, full-size workloads (sampled rows) --------------------------------
+
+def _full_size_check(case, heads):
+    x = W.dense_inputs(case)
+    o, lse = run_fwd(x.q, x.k, x.v, case.B, case.H, case.Hkv, case.N, case.d, case.scale, int(case.causal))
+    rows = sample_rows(case.N)
+    o_np = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    lse_np = lse.cpu().numpy()
+    del o, lse
+    group = case.H // case.Hkv
+    for (b, h) in heads:
+        g = h // group
+        O_ref, L_ref = oracle.attention_forward(x.f64("q", (slice(b, b + 1), slice(h, h + 1))),
+                                                x.f64("k", (slice(b, b + 1), slice(g, g + 1))),
+                                                x.f64("v", (slice(b, b + 1), slice(g, g + 1))),
+                                                case.scale, case.causal, rows=rows)
+        got = bf16_bits_to_f64(o_np[b, h, rows])
+        assert_bf16(got, O_ref[0, 0], f"{case.name} b={b} h={h}")
+        assert_lse(lse_np[b, h, rows], L_ref[0, 0], f"{case.name} b={b} h={h}")
+    # every output finite
+    assert np.isfinite(bf16_bits_to_f64(o_np[:, :, ::97])).all()
+    assert np.isfinite(lse_np).all()
+
+
+def test_full_prefill_d64_causal():
+    _need_gpu()
+    _full_size_check(W.PREFILL_D64, [(0, 0), (0, 13), (0, 31)])
+
+
+@pytest.mark.parametrize("case", [W.PREFILL_D128_CAUSAL, W.PREFILL_D128_FULL], ids=lambda c: c.name)
+def test_full_prefill_d128(case):
+    _need_gpu()
+    _full_size_check(case, [(0, 0), (3, 17), (7, 31)])
+
+
+def test_full_prefill_long_causal():
+    _need_gpu()
+    _full_size_check(W.PREFILL_LONG, [(0, 0), (0, 21)])
+
+
+# --- decode ----------------------------------------------------------------------------
+
+def run_decode(x: W.DecodeInputs, splits: int):
+    c = x.case
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
+    sl = to_dev(x.seqlens)
+    o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
+    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, c.Lmax, c.d, splits)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    fa.attn_decode(q, k, v, sl, o, lse, c.B, c.H, c.Hkv, c.Lmax, c.d, c.scale, splits, ws, nbytes)
+    torch.cuda.synchronize()
+    return bf16_dev_to_f64(o), lse.cpu().numpy()
+
+
+def decode_ref(x: W.DecodeInputs, batches=None):
+    c = x.case
+    batches = range(c.B) if batches is None else batches
+    O, L = [], []
+    for b in batches:
+        n = int(x.seqlens[b])
+        kk = bf16_bits_to_f64(x.k[b:b + 1, :, :n])
+        vv = bf16_bits_to_f64(x.v[b:b + 1, :, :n])
+        Ob, Lb = oracle.decode(bf16_bits_to_f64(x.q[b:b + 1]), kk, vv, np.array([n]), c.scale)
+        O.append(Ob[0])
+        L.append(Lb[0])
+    return np.stack(O), np.stack(L)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 7, 64])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_small(splits, G):
+    _need_gpu()
+    Hkv = 2
+    c = W.Decode("decode_small", 4, G * Hkv, Hkv, 700, 128, 1 / math.sqrt(128), 1, 700, 31)
+    x = W.decode_inputs(c, seqlens=[1, 17, 513, 700])
+    o, lse = run_decode(x, splits)
+    O_ref, L_ref = decode_ref(x)
+    assert_bf16(o, O_ref, f"G={G} splits={splits}")
+    assert_lse(lse, L_ref, f"G={G} splits={splits}")
+
+
+def test_decode_zero_length_sequence():
+    _need_gpu()
+    c = W.Decode("decode_empty", 2, 8, 2, 64, 128, 0.1, 1, 64, 32)
+    x = W.decode_inputs(c, seqlens=[0, 40])
+    o, lse = run_decode(x, 0)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    O_ref, L_ref = decode_ref(x, [1])
+    assert_bf16(o[1:], O_ref)
+    assert_lse(lse[1:], L_ref)
+
+
+@pytest.mark.parametrize("splits", [0, 16, 64])
+def test_full_decode_gqa(splits):
+    _need_gpu()
+    x = W.decode_inputs(W.DECODE_GQA)
+    o, lse = run_decode(x, splits)
+    O_ref, L_ref = decode_ref(x)
+    assert_bf16(o, O_ref, f"decode splits={splits}")
+    assert_lse(lse, L_ref, f"decode splits={splits}")
+
+
+# --- jagged HSTU -------------------------------------------------------------------------
+
+def run_hstu(x: W.JaggedInputs, causal: int):
+    c = x.case
+    T = int(x.offsets[-1])
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
+    off = to_dev(x.offsets)
+    o = torch.full((T, c.H, c.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fa.attn_hstu_jagged(q, k, v, o, off, len(x.lengths), c.H, c.d, x.max_seqlen, c.alpha, c.inv_n, causal)
+    torch.cuda.synchronize()
+    return bf16_dev_to_f64(o)
+
+
+def hstu_ref(x: W.JaggedInputs, causal: bool, seqs=None):
+    c = x.case
+    seqs = range(len(x.lengths)) if seqs is None else seqs
+    out = {}
+    for b in seqs:
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        sub = np.array([0, e - s], dtype=np.int64)
+        out[b] = oracle.hstu_jagged(bf16_bits_to_f64(x.q[s:e]), bf16_bits_to_f64(x.k[s:e]),
+                                    bf16_bits_to_f64(x.v[s:e]), sub, c.alpha, c.inv_n, causal)
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_hstu_small_every_element(d, causal):
+    _need_gpu()
+    c = W.Jagged("hstu_small", 6, 3, d, 1, 300, 0.3, 1.0 / 64, bool(causal), 41, 1.0)
+    x = W.jagged_inputs(c, lengths=[5, 0, 1, 129, 300, 64])
+    o = run_hstu(x, causal)
+    ref = hstu_ref(x, bool(causal))
+    for b, r in ref.items():
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
+
+
+def test_full_hstu_jagged():
+    _need_gpu()
+    c = W.HSTU_JAGGED
+    x = W.jagged_inputs(c)
+    o = run_hstu(x, 1)
+    assert np.isfinite(o).all()
+    longest = int(np.argmax(x.lengths))
+    seqs = sorted({0, 1, longest, len(x.lengths) - 1})
+    ref = hstu_ref(x, True, seqs)
+    for b, r in ref.items():
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
