@@ -1,0 +1,321 @@
+#!/usr/bin/env python
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+
+  1. attn_fwd     causal prefill, B=8, H=32, N=4096, d=128, bf16  (headline)
+  2. attn_decode  GQA decode, B=16, H=32, Hkv=8, L_b in [16384, 32768], d=128
+  3. attn_hstu_jagged  16 jagged sequences, L_b in [512, 4096], H=4, d=64
+
+``value`` is the prefill throughput in TFLOP/s with the FLOP convention of the
+ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
+prefill launch on the stream the kernel runs on; decode GB/s and HSTU TFLOP/s
+are reported beside it.  Prints ONE JSON line.
+
+Other modes (used for profiling, see profiles/):
+  --only prefill|decode|hstu   run just that part of the step
+  --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
+  --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
+  --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TILE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/tile_bf16.hip", "exact_attention_11_amd/csrc/common.hpp",
+                       "exact_attention_11_amd/csrc/launch.hpp"]
+DECODE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/decode.hip", "exact_attention_11_amd/csrc/common.hpp",
+                         "exact_attention_11_amd/csrc/launch.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_bf16_prefill_d128_causal_traffic.txt")
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["prefill", "decode", "hstu"], default=None)
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    return ap.parse_args(argv)
+
+
+# ----------------------------------------------------------------------------- rocprofv3 summaries
+
+def _read_csv(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(d: str) -> None:
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    for path in files:
+        rows = _read_csv(path)
+        print(f"# {os.path.relpath(path, d)}")
+        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel")
+        for r in rows:
+            name = r.get("Name", r.get("KernelName", "?"))
+            print(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                  f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {name[:110]}")
+
+
+def summarize_pmc(d: str) -> None:
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    agg = {}
+    for path in files:
+        for r in _read_csv(path):
+            name = r.get("Kernel_Name", "?")
+            ctr = r.get("Counter_Name", "?")
+            val = float(r.get("Counter_Value", "nan"))
+            key = (name, ctr)
+            disp = r.get("Dispatch_Id", "")
+            agg.setdefault(key, {})
+            agg[key][disp] = agg[key].get(disp, 0.0) + val
+    print(f"{'dispatches':>10} {'mean_per_dispatch':>18} {'unit':>5}  counter  kernel")
+    for (name, ctr), per in sorted(agg.items()):
+        vals = list(per.values())
+        mean = sum(vals) / len(vals)
+        print(f"{len(vals):10d} {mean:18.1f} {'KiB' if ctr.endswith('SIZE') else '':>5}  {ctr}  {name[:100]}")
+
+
+# ----------------------------------------------------------------------------- the benchmark
+
+def read_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary,
+    or None when the tile kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha") != sources_sha(TILE_KERNEL_SOURCES):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, case, seconds: float):
+    """The fp64 oracle as it stands, on a bounded sample of the prefill
+    workload: whole (b, h) heads, all rows, until about `seconds` elapsed."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        g = h // (case.H // case.Hkv)
+        q = x.f64("q", (slice(b, b + 1), slice(h, h + 1)))
+        k = x.f64("k", (slice(b, b + 1), slice(g, g + 1)))
+        v = x.f64("v", (slice(b, b + 1), slice(g, g + 1)))
+        oracle.attention_forward(q, k, v, case.scale, case.causal)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    per_head = 2 * case.N * case.N * case.d * (1 if case.causal else 2)
+    return {
+        "value": round(done * per_head / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (b,h) heads of the B={case.B} H={case.H} N={case.N} d={case.d} "
+                  f"{'causal' if case.causal else 'non-causal'} prefill, all rows, fp64 numpy, {el:.1f} s",
+    }
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is described "
+              "in DESIGN.md and not built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_attention_11_amd as fa
+    from synthgen import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
+        return 0
+
+    parts = [args.only] if args.only else ["prefill", "decode", "hstu"]
+    print(f"bench: preparing inputs for {parts}", file=sys.stderr, flush=True)
+
+    pc = W.PREFILL_D128_CAUSAL
+    px = W.dense_inputs(pc) if "prefill" in parts or not args.no_cpu_baseline else None
+    calls = {}
+    if "prefill" in parts:
+        q, k, v = bf16(px.q), bf16(px.k), bf16(px.v)
+        o = torch.empty((pc.B, pc.H, pc.N, pc.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((pc.B, pc.H, pc.N), dtype=torch.float32, device=dev)
+        calls["prefill"] = lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 1)
+    dc = W.DECODE_GQA
+    dx = None
+    if "decode" in parts:
+        dx = W.decode_inputs(dc)
+        dq, dk, dv = bf16(dx.q), bf16(dx.k), bf16(dx.v)
+        dsl = torch.from_numpy(dx.seqlens).to(dev)
+        do = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty((dc.B, dc.H), dtype=torch.float32, device=dev)
+        wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, args.splits)
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+        calls["decode"] = lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
+                                                 dc.scale, args.splits, ws, wsb)
+    jc = W.HSTU_JAGGED
+    jx = None
+    if "hstu" in parts:
+        jx = W.jagged_inputs(jc)
+        T = int(jx.offsets[-1])
+        jq, jk, jv = bf16(jx.q), bf16(jx.k), bf16(jx.v)
+        joff = torch.from_numpy(jx.offsets).to(dev)
+        jo = torch.empty((T, jc.H, jc.d), dtype=torch.bfloat16, device=dev)
+        nseq = len(jx.lengths)
+        calls["hstu"] = lambda: fa.attn_hstu_jagged(jq, jk, jv, jo, joff, nseq, jc.H, jc.d, jx.max_seqlen,
+                                                    jc.alpha, jc.inv_n, 1)
+
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        for name in parts:
+            if record is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[name]()
+                e1.record(stream)
+                record[name].append((e0, e1))
+            else:
+                calls[name]()
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = {name: [] for name in parts}
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: sum(a.elapsed_time(b) for a, b in rec[name]) / max(1, len(rec[name])) for name in parts}
+
+    out = {
+        "metric": "attn fwd TFLOPS & % bf16 MFMA peak (N=4096,d=128 causal); decode HBM GB/s",
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / max(1, args.steps), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill B=8 H=32 N=4096 d=128 bf16 (+ GQA decode, jagged HSTU in the step)",
+                   "global_batch": pc.B, "seq_len": pc.N, "parallelism": "none (1 GPU)"},
+    }
+    if "prefill" in parts:
+        flops = 2 * pc.N * pc.N * pc.d * pc.B * pc.H
+        tflops = flops / (ms["prefill"] * 1e-3) / 1e12
+        out["value"] = round(tflops, 2)
+        traffic = read_traffic()
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "kernel": "tile_kernel<128,causal,softmax>", "flops_per_launch": flops,
+                           "ms_per_launch": round(ms["prefill"], 4)}
+    if "decode" in parts:
+        ssum = int(dx.seqlens.sum())
+        nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
+        gbs = nbytes / (ms["decode"] * 1e-3) / 1e9
+        out["decode"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                         "ms_per_call": round(ms["decode"], 4), "algorithmic_bytes": nbytes, "sum_L": ssum,
+                         "splits": args.splits or "auto"}
+        if out["value"] is None:
+            out.update({"value": round(gbs, 1), "unit": "GB/s"})
+    if "hstu" in parts:
+        hf = sum(2 * int(L) * int(L) * jc.d for L in jx.lengths) * jc.H
+        ht = hf / (ms["hstu"] * 1e-3) / 1e12
+        out["hstu"] = {"TFLOP/s": round(ht, 2), "frac_bf16_peak": round(ht / PEAK_BF16_TFLOPS, 4),
+                       "ms_per_call": round(ms["hstu"], 4), "flops": hf}
+        if out["value"] is None:
+            out.update({"value": round(ht, 2), "unit": "TFLOP/s"})
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(px, pc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

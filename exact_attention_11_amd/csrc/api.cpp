@@ -5,6 +5,7 @@
 // exception crosses the ABI and no device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -83,6 +84,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (st != FATTN_OK) return st;
   if (d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "attn_fwd: d=%d not supported (64 or 128)", d);
   if (B == 0 || N == 0) return ok();
+  // K/V rows of one head are addressed with 32-bit byte offsets
+  if ((double)N * d * 2 >= 4294967296.0) return fail(FATTN_ERR_INVALID_ARG, "attn_fwd: N*d too large for one head");
   fattn::TileArgs a{};
   a.q = q;
   a.k = k;
@@ -95,7 +98,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.Hkv = Hkv;
   a.N = N;
   a.d = d;
-  a.c = scale * kLog2e;
+  // scale == 0 runs as the smallest normal scale: for any finite score s,
+  // s * FLT_MIN * log2(e) rounds away against 1 in exp2, so every visible
+  // weight is exactly 1 (the scale-0 result), and masked scores (-inf) still
+  // give weight exactly 0.
+  a.c = std::fmax(scale * kLog2e, FLT_MIN);
   a.inv_n = 1.f;
   a.causal = causal;
   a.epi = fattn::Epilogue::Softmax;
@@ -198,6 +205,9 @@ int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o, const
     return fail(FATTN_ERR_INVALID_ARG, "%s: q, k, v, o and offsets must be non-null", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  // rows of one sequence are addressed with 32-bit byte offsets
+  if ((double)max_seqlen * H * d * 2 >= 4294967296.0)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: max_seqlen*H*d too large", fn);
   fattn::TileArgs a{};
   a.q = q;
   a.k = k;

@@ -48,11 +48,47 @@ __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return per
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resource over [base, base + bytes): loads at byte offsets >= bytes
+// return zero (hardware range check), so tails need no predication.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// output lane i, element t is element (i % 4) of the 8 bytes addressed by
+// lane 4t + i/4 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
+// a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, f32 result (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) as bf16
 __device__ __forceinline__ void stg8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Value held by lane (lane ^ 32) of the wave.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: each lane ends up
+// with its own value in one result and its partner's in the other).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 

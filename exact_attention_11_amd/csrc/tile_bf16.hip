@@ -15,10 +15,15 @@
 //
 // Keys are fed to the first product in a permuted row order (bits 2 and 3 of the
 // in-block key index swapped) so that each lane's 8 P values for one K=16 step
-// of the second product are 8 CONSECUTIVE keys; V^T can then be read from LDS
-// with one 16-byte load per step.  V is transposed while it is written into LDS
-// (register byte-permutes), with a row-dependent XOR swizzle of 16-byte chunks
-// so that the 16-byte reads are bank-conflict free.
+// of the second product are 8 CONSECUTIVE keys.  V stays in its natural
+// [key][d] layout in LDS and the V^T operand is gathered with the transposing
+// LDS read (ds_read_b64_tr_b16): two reads give a lane 8 consecutive keys of
+// one d column.  V rows are XOR-swizzled in 16-byte chunks so that the four key
+// rows one read touches fall in different banks.
+//
+// K and V tiles are fetched with buffer loads whose descriptor covers only the
+// valid rows of the sequence: rows past the end read as zero, so no load is
+// predicated.
 //
 // Two pointwise epilogues share the loop:
 //  * Softmax: online softmax with a running row max m and running sum l
@@ -36,7 +41,7 @@
 // below the diagonal run unmasked, tiles straddling it are masked per element,
 // tiles wholly above it are never loaded or computed (HSTU page, optimisation
 // two).  Rows and keys past the sequence end (ragged N, jagged sequences) are
-// masked the same way and their loads are predicated off.
+// masked the same way.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,15 +67,14 @@ template <int D, int BN>
 struct Lds {
   static constexpr int kRow = (D + 8) * 2;  // K row: D bf16 + 16-byte pad
   static constexpr int kBytes = BN * kRow;
-  static constexpr int vRow = BN * 2;       // V^T row: BN bf16, swizzled
-  static constexpr int vBytes = D * vRow;
+  static constexpr int vRow = D * 2;        // V row: D bf16, 16-byte chunks swizzled
+  static constexpr int vBytes = BN * vRow;
   static constexpr int stage = kBytes + vBytes;
   static constexpr int total = 2 * stage;
-  // XOR applied to the 16-byte chunk index of V^T row m: rows that share a
-  // 256-byte bank line get different chunk orders.
-  __device__ static __forceinline__ int vswz(int m) {
-    return BN == 64 ? ((m >> 1) & 7) : (m & 15);
-  }
+  // XOR applied to the 16-byte chunk index of V row r: the 4 consecutive rows a
+  // transposing read touches land on disjoint banks (bits >= 2 of the chunk
+  // index only, so 32-byte pieces stay contiguous).
+  __device__ static __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
 };
 
 // In-block key order of the first product: swap bits 2 and 3.
@@ -156,55 +160,47 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
     qf[c] = as_bf16x8(t);
   }
 
-  // ---- global -> register staging of one K/V tile
-  constexpr int KCH = D / 8;                     // 16-byte chunks per K row
-  constexpr int KLOADS = BN * KCH / kThreads;    // 4
-  const int vkg = tid % (BN / 4);                // V: 4 keys x 8 d per thread
-  const int vdg = tid / (BN / 4);
-  u32x4 kr[KLOADS], vr[4];
+  // ---- global -> register staging of one K/V tile (buffer loads; rows past
+  // the sequence end read as zero)
+  constexpr int KCH = D / 8;                   // 16-byte chunks per row
+  constexpr int NLD = BN * KCH / kThreads;     // 16-byte loads per thread per tensor
+  const uint32_t row_bytes = (uint32_t)row_stride * 2;
+  uint32_t goff[NLD];  // byte offset of this thread's chunks within a tile
+  int lds_row[NLD], lds_chunk[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ci = tid + kThreads * i;
+    lds_row[i] = ci / KCH;
+    lds_chunk[i] = ci % KCH;
+    goff[i] = (uint32_t)lds_row[i] * row_bytes + (uint32_t)lds_chunk[i] * 16u;
+  }
+  u32x4 kr[NLD], vr[NLD];
 
   auto load_tile = [&](int k0) {
+    // valid bytes from row k0: rows k0 .. len-1 of this head
+    const uint32_t bytes = (uint32_t)(len - k0 - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * row_stride, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * row_stride, bytes);
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = k0 + ci / KCH;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (row < len) t = ldg16(kp + (long)row * row_stride + (ci % KCH) * 8);
-      kr[i] = t;
-    }
+    for (int i = 0; i < NLD; ++i) kr[i] = buf_load16(rk, goff[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = k0 + 4 * vkg + i;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (row < len) t = ldg16(vp + (long)row * row_stride + vdg * 8);
-      vr[i] = t;
-    }
+    for (int i = 0; i < NLD; ++i) vr[i] = buf_load16(rv, goff[i]);
   };
   auto store_tile = [&](int buf) {
     unsigned char* sk = smem + buf * L::stage;
     unsigned char* sv = sk + L::kBytes;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int ci = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(sk + (ci / KCH) * L::kRow + (ci % KCH) * 16) = kr[i];
-    }
-    const int chunk = vkg >> 1;
-    const int half = vkg & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int m = 8 * vdg + e;
-      const int w = e >> 1;
-      u32x2 t;
-      if (e & 1) {
-        t[0] = pair_hi(vr[0][w], vr[1][w]);
-        t[1] = pair_hi(vr[2][w], vr[3][w]);
-      } else {
-        t[0] = pair_lo(vr[0][w], vr[1][w]);
-        t[1] = pair_lo(vr[2][w], vr[3][w]);
-      }
-      *reinterpret_cast<u32x2*>(sv + m * L::vRow + ((chunk ^ L::vswz(m)) << 4) + (half << 3)) = t;
+    for (int i = 0; i < NLD; ++i) {
+      *reinterpret_cast<u32x4*>(sk + lds_row[i] * L::kRow + lds_chunk[i] * 16) = kr[i];
+      *reinterpret_cast<u32x4*>(sv + lds_row[i] * L::vRow + ((lds_chunk[i] ^ L::vswz(lds_row[i])) << 4)) = vr[i];
     }
   };
+
+  // per-lane part of the transposing V^T reads: row offset within the 8-key
+  // group and (chunk, byte) of the 4 d values this lane addresses
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
 
   // ---- accumulators and running statistics
   f32x16 acc[NDB];
@@ -233,40 +229,41 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
       // S^T = K Q^T
       f32x16 s[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
       for (int c = 0; c < NDC; ++c) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const u32x4 kf = *reinterpret_cast<const u32x4*>(
               sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], s[kb], 0, 0, 0);
+          const f32x16 zero = {};
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
         }
       }
 
       const bool masked = (CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len);
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * kb + acc_key(e, g2);
-            const bool vis = (key < len) && (!CAUSAL || key <= qrow);
-            if (!vis) s[kb][e] = kNegInf;
-          }
-      }
+      // visibility of accumulator element e of 32-key block kb
+      auto visible = [&](int kb, int e) {
+        const int key = k0 + 32 * kb + acc_key(e, g2);
+        return (key < len) && (!CAUSAL || key <= qrow);
+      };
 
       uint32_t pk[NKB][8];  // bf16 pairs of P (or of silu scores)
       if constexpr (EPI == Epilogue::Softmax) {
+        // Masked scores become -inf; with cexp > 0 (the host never passes 0)
+        // their weights exp2(-inf) are exactly 0, with no per-element select.
+        if (masked) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (!visible(kb, e)) s[kb][e] = kNegInf;
+        }
         float mt = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-        mt = fmaxf(mt, xor32(mt));
-        const float mts = (mt == kNegInf) ? kNegInf : mt * cexp;
+        mt = max_xor32(mt);
+        const float mts = mt * cexp;  // -inf stays -inf
         if (wave_any(mts > m_ref + kRescaleSlack)) {
           const float mn = fmaxf(m_ref, mts);
           const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m_ref - mn);
@@ -284,7 +281,6 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             p[e] = exp2_hw(__builtin_fmaf(s[kb][e], cexp, nm));
-            if (masked) p[e] = (s[kb][e] == kNegInf) ? 0.f : p[e];
             l_part += p[e];
           }
 #pragma unroll
@@ -292,32 +288,43 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
         }
       } else {
         const float alpha = cexp;
+        float y[NKB][16];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float y[16];
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const float x = s[kb][e] * alpha;
-            y[e] = x * rcp_hw(1.f + exp2_hw(-x * kLog2e));
-            if (masked) y[e] = (s[kb][e] == kNegInf) ? 0.f : y[e];
+            y[kb][e] = x * rcp_hw(1.f + exp2_hw(-x * kLog2e));
           }
+        if (masked) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (!visible(kb, e)) y[kb][e] = 0.f;
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[kb][2 * e], y[kb][2 * e + 1]);
       }
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; V^T fragments gathered by transposing reads
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
           const bf16x8 pb = as_bf16x8(pw);
-          const int chunk = 4 * kb + 2 * jj + g2;
+          const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
+          const unsigned char* vrow = sv + krow * L::vRow;
+          const int swz = L::vswz(krow);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int m = 32 * db + n32;
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + m * L::vRow + ((chunk ^ L::vswz(m)) << 4));
+            const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
+            const u32x2 lo = lds_read_tr16(addr);
+            const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
           }
         }
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
 
   float scale_out;
   if constexpr (EPI == Epilogue::Softmax) {
-    const float lt = l_part + xor32(l_part);
+    const float lt = sum_xor32(l_part);
     scale_out = lt > 0.f ? 1.f / lt : 0.f;
     if (a.lse != nullptr && g2 == 0) {
       a.lse[lse_base + qrow] = lt > 0.f ? (m_ref + log2_hw(lt)) * kLn2 : kNegInf;

@@ -6,11 +6,13 @@ their inputs from here so that they see the very same bits.
 
 Recipe (one stream per tensor):
 
-* generator: numpy's PCG64 seeded with ``SeedSequence([seed, tensor_id])``
-  (tensor ids: Q=1, K=2, V=3, lengths=4), so each tensor has its own stream
-  and drawing one tensor never shifts another;
-* values: ``sigma * standard_normal`` drawn in float64, rounded to float32
-  (round-to-nearest-even), then to bfloat16 (round-to-nearest-even) where the
+* generator: numpy's PCG64.  A tensor is drawn in chunks of 2^22 values;
+  chunk c of tensor ``tensor_id`` uses ``SeedSequence([seed, tensor_id, c])``
+  (tensor ids: Q=1, K=2, V=3, lengths=4), so every tensor and chunk has its
+  own stream, drawing one never shifts another, and chunks can be drawn in
+  parallel threads;
+* values: ``sigma * standard_normal`` drawn in float32 (numpy's float32
+  ziggurat), then rounded to bfloat16 (round-to-nearest-even) where the
   workload stores bf16;
 * lengths: integers uniform on the closed interval ``[lo, hi]``.
 
@@ -22,6 +24,8 @@ jagged sequences with per-sequence lengths (the HSTU page, optimisation three
 """
 
 from __future__ import annotations
+
+import os
 
 import numpy as np
 
@@ -57,22 +61,44 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def normal_f32(seed: int, tensor_id: int, shape, sigma: float = 1.0) -> np.ndarray:
-    """i.i.d. N(0, sigma^2) values rounded to float32."""
-    g = _rng(seed, tensor_id)
+_CHUNK = 1 << 22
+
+
+def _chunk_rng(seed: int, tensor_id: int, c: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tensor_id), int(c)])))
+
+
+def _draw(seed: int, tensor_id: int, shape, sigma: float, to_bf16: bool) -> np.ndarray:
     n = int(np.prod(shape))
-    # Draw in chunks to bound the float64 temporary for large tensors.
-    out = np.empty(n, dtype=np.float32)
-    chunk = 1 << 24
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = (g.standard_normal(e - s) * sigma).astype(np.float32)
+    out = np.empty(n, dtype=np.uint16 if to_bf16 else np.float32)
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+
+    def work(c: int) -> None:
+        s0, s1 = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        z = _chunk_rng(seed, tensor_id, c).standard_normal(s1 - s0, dtype=np.float32)
+        if sigma != 1.0:
+            z *= np.float32(sigma)
+        out[s0:s1] = f32_to_bf16_bits(z) if to_bf16 else z
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, nchunks)) as ex:
+            list(ex.map(work, range(nchunks)))
     return out.reshape(shape)
+
+
+def normal_f32(seed: int, tensor_id: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """i.i.d. N(0, sigma^2) values in float32."""
+    return _draw(seed, tensor_id, shape, sigma, False)
 
 
 def normal_bf16(seed: int, tensor_id: int, shape, sigma: float = 1.0) -> np.ndarray:
     """i.i.d. N(0, sigma^2) values rounded to bfloat16; returns uint16 bit patterns."""
-    return f32_to_bf16_bits(normal_f32(seed, tensor_id, shape, sigma))
+    return _draw(seed, tensor_id, shape, sigma, True)
 
 
 def uniform_lengths(seed: int, count: int, lo: int, hi: int) -> np.ndarray:
