@@ -18,6 +18,9 @@ Other modes (used for profiling, see profiles/):
   --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
   --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
   --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
+  --traffic FETCH WRITE CFETCH CWRITE
+                               HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE
+                               runs, calibrated by the same counters on a 1 GiB copy
 """
 
 from __future__ import annotations
@@ -56,7 +59,7 @@ def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["prefill", "decode", "hstu"], default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +67,7 @@ def parse_args(argv=None):
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
     return ap.parse_args(argv)
 
 
@@ -109,6 +113,36 @@ def summarize_pmc(d: str) -> None:
         vals = list(per.values())
         mean = sum(vals) / len(vals)
         print(f"{len(vals):10d} {mean:18.1f} {'KiB' if ctr.endswith('SIZE') else '':>5}  {ctr}  {name[:100]}")
+
+
+def _pmc_mean_kib(d: str, kernel_substr: str, counter: str) -> float:
+    vals = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in _read_csv(path):
+            if kernel_substr in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+                k = r.get("Dispatch_Id", "")
+                vals[k] = vals.get(k, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} for {kernel_substr!r} under {d}")
+    return sum(vals.values()) / len(vals)
+
+
+def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir) -> None:
+    """Print the traffic summary for the causal d=128 prefill kernel: counter KiB
+    per dispatch scaled so that a 1 GiB device copy reads and writes 1 GiB."""
+    kern = "tile_kernel<128, true, (fattn::Epilogue)0, false>"
+    copy = "copyBuffer"
+    gib = float(1 << 30)
+    f_cal = gib / (_pmc_mean_kib(cfetch_dir, copy, "FETCH_SIZE") * 1024.0)
+    w_cal = gib / (_pmc_mean_kib(cwrite_dir, copy, "WRITE_SIZE") * 1024.0)
+    fetch = _pmc_mean_kib(fetch_dir, kern, "FETCH_SIZE") * 1024.0 * f_cal
+    write = _pmc_mean_kib(write_dir, kern, "WRITE_SIZE") * 1024.0 * w_cal
+    print(f"fetch_calibration: {f_cal:.4f}")
+    print(f"write_calibration: {w_cal:.4f}")
+    print(f"hbm_fetch_bytes_per_launch: {fetch:.0f}")
+    print(f"hbm_write_bytes_per_launch: {write:.0f}")
+    print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
+    print(f"kernel_sources_sha: {sources_sha(TILE_KERNEL_SOURCES)}")
 
 
 # ----------------------------------------------------------------------------- the benchmark
@@ -174,6 +208,9 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.traffic:
+        traffic_summary(*args.traffic)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is described "

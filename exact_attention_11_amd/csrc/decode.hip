@@ -1,21 +1,23 @@
-// Split-KV decode attention with a log-sum-exp combine, on the vector ALUs.
+// Split-KV decode attention with a log-sum-exp combine.
 //
 // Decode reads every cached key and value once per step and does O(n d) work,
 // so it is bound by HBM bandwidth, not by the matrix units (ledger page,
-// bandwidth section).  The design therefore only tries to keep enough bytes in
+// bandwidth section).  The design therefore only tries to keep many bytes in
 // flight and to touch each byte once:
 //
-//  * kernel 1, one workgroup per (sequence, kv-head, split): the split owns a
-//    contiguous chunk of cache rows.  The G query heads that share the kv-head
-//    (grouped-query attention) are served by the same pass, so K and V are
-//    streamed once per kv-head.  Each 16-lane row group of a wave handles one
-//    key: lane i holds 8 consecutive d values (one 16-byte load), dot products
-//    use v_dot2_f32_bf16 and a 4-step DPP butterfly within the row.  Scores of
-//    a sub-chunk go to LDS, then max and exponentials (base 2), then V is
-//    streamed and p * v accumulated in f32.  Sub-chunks are merged online
-//    (running max and sum, as in the prefill kernel).  The normalised partial
-//    output and its natural-log LSE go to the workspace; an empty chunk
-//    writes 0 and -inf.
+//  * kernel 1, one 64-wide wave per (sequence, kv-head, split): the split owns
+//    a contiguous chunk of cache rows.  The G query heads that share the
+//    kv-head (grouped-query attention) are served by the same pass, so K and V
+//    are streamed once per kv-head.  The G heads are the columns of small
+//    matrix-core products (16x16x32 bf16): scores S^T = K Q^T and output
+//    O^T += V^T P^T, with V^T gathered from LDS by transposing reads.  The
+//    matrix cores are mostly idle doing this, but they take the dot products
+//    off the vector ALUs so that the wave spends its time waiting on HBM, not
+//    computing.  Online softmax per head (base 2, rescaled only when a score
+//    exceeds the reference max by more than 2^8).  The next block's loads are
+//    issued as soon as the current block's registers are consumed.  The
+//    normalised partial output and its natural-log LSE go to the workspace; an
+//    empty chunk writes 0 and -inf.
 //  * kernel 2, one workgroup per (sequence, head): weights exp(lse_c - lse)
 //    with lse = log-sum-exp over the splits, O = sum_c w_c o_c.
 #include "common.hpp"
@@ -25,24 +27,8 @@ namespace fattn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kSub = 512;    // keys per scored sub-chunk
-constexpr int kUnroll = 8;   // 16-key steps issued back to back
-constexpr int kThreads = 256;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)); // half-row mirror
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)); // row mirror
-  return x;
-}
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kCombineWaves = 4;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -55,17 +41,26 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int chunk) {
-  __shared__ float sc[G][kSub];
-  __shared__ float stat[G][2];
-  __shared__ float red[4][G][kD];
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int kk = 4 * wv + (lane >> 4);  // key slot within a 16-key step
-  const int ds = lane & 15;             // 8-wide d slice
+// XOR on the 16-byte chunk index of V row r in LDS: the 8 rows one
+// transposing read touches (4 per 16-lane group, two groups per LDS cycle)
+// land on disjoint banks; bit 0 is never flipped, so 32-byte pieces stay whole.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | (((r >> 2) & 1) << 1); }
+
+// One 64-wide wave per (sequence, kv-head, split).  Blocks of 32 keys:
+//   S^T[32 keys x 16 cols] = K Q^T   (v_mfma_f32_16x16x32_bf16, 2 x 4 steps;
+//                                      column n < G is query head h0 + n, the
+//                                      other columns multiply zeros)
+//   online softmax per column on the accumulator (8 scores per lane)
+//   O^T[128 d x 16 cols] += V^T P^T   (8 steps; V^T from LDS by transposing
+//                                      reads, P^T straight from the scores)
+template <int G>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chunk) {
+  __shared__ __attribute__((aligned(16))) unsigned char sv[32 * kD * 2];
+  const int lane = threadIdx.x;
+  const int n16 = lane & 15;  // column (query head) of the 16x16 tiles
+  const int g4 = lane >> 4;   // 16-lane group
 
   const int S = a.splits;
   int wid = blockIdx.x;
@@ -84,227 +79,213 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   float* pl = a.part_lse + ((long)b * a.H + h0) * S + s;       // head hh at + hh*S
 
   if (kb0 >= kb1) {
-    for (int i = tid; i < G * kD; i += kThreads) po[(long)(i / kD) * S * kD + (i % kD)] = 0.f;
-    if (tid < G) pl[(long)tid * S] = kNegInf;
+    for (int i = lane; i < G * kD; i += 64) po[(long)(i / kD) * S * kD + (i % kD)] = 0.f;
+    if (lane < G) pl[(long)lane * S] = kNegInf;
     return;
   }
 
-  const long kvbase = ((long)b * a.Hkv + g) * a.Lmax * kD;
-  const uint16_t* kp = (const uint16_t*)a.k + kvbase + 8 * ds;
-  const uint16_t* vp = (const uint16_t*)a.v + kvbase + 8 * ds;
+  // rows [kb0, kb1) of this kv-head; loads past kb1 read zero
+  const long rowbase = ((long)b * a.Hkv + g) * a.Lmax + kb0;
+  const uint32_t bytes = (uint32_t)(kb1 - kb0) * (kD * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + rowbase * kD, bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + rowbase * kD, bytes);
+  const int n = kb1 - kb0;
 
-  uint32_t qv[G][4];
+  // Q^T operand: column n16 = head h0 + n16 (zero for n16 >= G), d = 32c + 8*g4 .. +8
+  bf16x8 qf[4];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const u32x4 t = ldg16((const uint16_t*)a.q + ((long)b * a.H + h0 + hh) * kD + 8 * ds);
-    qv[hh][0] = t[0];
-    qv[hh][1] = t[1];
-    qv[hh][2] = t[2];
-    qv[hh][3] = t[3];
+  for (int c = 0; c < 4; ++c) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (n16 < G) t = ldg16((const uint16_t*)a.q + ((long)b * a.H + h0 + n16) * kD + 32 * c + 8 * g4);
+    qf[c] = as_bf16x8(t);
   }
 
-  float acc[G][8];
-  float m_run[G], l_run[G];
+  f32x4v acc[8];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m_run[hh] = kNegInf;
-    l_run[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  }
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;  // running (base-2, scaled) max of column n16
+  float l = 0.f;      // this lane's share of the running sum
   const float c = a.c;
 
-  for (int sb = kb0; sb < kb1; sb += kSub) {
-    const int se = min(kb1, sb + kSub);
-    const int n = se - sb;
+  // per-lane offsets: K operand rows n16 and 16 + n16 of a block, d = 32c + 8*g4;
+  // V rows g4 + 4i (i = 0..7), d = 8*n16 .. +8
+  const uint32_t koff = (uint32_t)n16 * (kD * 2) + 16u * g4;
+  const uint32_t voff = (uint32_t)g4 * (kD * 2) + 16u * n16;
+  // transposing reads: row 4*g4 + (lane&15)/4 (+16), d = 16*db + 4*(lane&3)
+  const int tr_r = 4 * g4 + (n16 >> 2);
 
-    // pass A: scaled base-2 scores of the sub-chunk into LDS
-    for (int base = sb; base < se; base += 16 * kUnroll) {
-      u32x4 kv[kUnroll];
+  u32x4 kr[8], vr[8];
+  auto issue = [&](int blk) {
+    const uint32_t o = (uint32_t)blk * (kD * 2);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int key = base + 16 * u + kk;
-        u32x4 t = {0u, 0u, 0u, 0u};
-        if (key < se) t = ldg16(kp + (long)key * kD);
-        kv[u] = t;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int key = base + 16 * u + kk;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          float p = dot2(qv[hh][0], kv[u][0], 0.f);
-          p = dot2(qv[hh][1], kv[u][1], p);
-          p = dot2(qv[hh][2], kv[u][2], p);
-          p = dot2(qv[hh][3], kv[u][3], p);
-          p = row16_sum(p);
-          if (ds == hh && key < se) sc[hh][key - sb] = p * c;
-        }
-      }
+    for (int c2 = 0; c2 < 4; ++c2) {
+      kr[c2] = buf_load16(rk, o + koff + 64u * c2);
+      kr[4 + c2] = buf_load16(rk, o + 16u * (kD * 2) + koff + 64u * c2);
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vr[i] = buf_load16(rv, o + voff + (uint32_t)(4 * i) * (kD * 2));
+  };
 
-    // sub-chunk max, exponentials and sum; wave wv serves heads wv, wv+4, ...
-    for (int hh = wv; hh < G; hh += 4) {
-      float mx = kNegInf;
-      for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[hh][i]);
-      mx = wave_max(mx);
-      // m_run is the same in every thread, so this wave can fix the new
-      // reference max for head hh and publish it with the sum below.
-      float sum = 0.f;
-      const float mnew = fmaxf(m_run[hh], mx);
-      for (int i = lane; i < n; i += 64) {
-        const float p = exp2_hw(sc[hh][i] - mnew);
-        sc[hh][i] = p;
-        sum += p;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        stat[hh][0] = mnew;
-        stat[hh][1] = sum;
-      }
+  issue(0);
+  for (int blk = 0; blk < n; blk += 32) {
+    // S^T for keys blk .. blk+15 (sa) and blk+16 .. blk+31 (sb)
+    f32x4v sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[c2]), qf[c2], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[4 + c2]), qf[c2], sb, 0, 0, 0);
     }
-    __syncthreads();
-
+    // V block -> LDS (natural [key][d] layout, swizzled chunks)
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float mnew = stat[hh][0];
-      const float alpha = (m_run[hh] == kNegInf) ? 0.f : exp2_hw(m_run[hh] - mnew);
-      m_run[hh] = mnew;
-      l_run[hh] = l_run[hh] * alpha + stat[hh][1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+    for (int i = 0; i < 8; ++i) {
+      const int r = g4 + 4 * i;
+      *reinterpret_cast<u32x4*>(sv + r * (kD * 2) + ((n16 ^ v_swz(r)) << 4)) = vr[i];
     }
+    if (blk + 32 < n) issue(blk + 32);
 
-    // pass B: stream V, accumulate p * v
-    for (int base = sb; base < se; base += 16 * kUnroll) {
-      u32x4 vv[kUnroll];
+    // scores of this lane: keys blk + 4*g4 + r (sa) and blk + 16 + 4*g4 + r (sb)
+    float sc[8];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int key = base + 16 * u + kk;
-        u32x4 t = {0u, 0u, 0u, 0u};
-        if (key < se) t = ldg16(vp + (long)key * kD);
-        vv[u] = t;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int key = base + 16 * u + kk;
-        const bool in = key < se;
-        float vf[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          vf[2 * w] = bf16_lo(vv[u][w]);
-          vf[2 * w + 1] = bf16_hi(vv[u][w]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float p = in ? sc[hh][min(key - sb, kSub - 1)] : 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, vf[e], acc[hh][e]);
-        }
-      }
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = (blk + 4 * g4 + r < n) ? sa[r] * c : kNegInf;
+      sc[4 + r] = (blk + 16 + 4 * g4 + r < n) ? sb[r] * c : kNegInf;
     }
-    __syncthreads();  // sc and stat are rewritten by the next sub-chunk
-  }
-
-  // reduce over the 4 key slots of a wave (lanes l, l^16, l^32, l^48) ...
+    float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = max_xor32(mt);
+    if (wave_any(mt > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m - mn);
+      m = mn;
+      l *= alpha;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    }
+    float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = acc[hh][e];
-      x += __shfl_xor(x, 16, 64);
-      x += __shfl_xor(x, 32, 64);
-      acc[hh][e] = x;
+      p[e] = exp2_hw(sc[e] - m);  // m is finite: every block has a valid key
+      l += p[e];
     }
-  // ... then over the 4 waves through LDS
-  if (lane < 16) {
+    const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    const bf16x8 pb = as_bf16x8(pw);
+
+    // O^T += V^T P^T: slots 0-3 = keys 4*g4 + t, slots 4-7 = keys 16 + 4*g4 + t
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wv][hh][8 * ds + e] = acc[hh][e];
+    for (int db = 0; db < 8; ++db) {
+      const int chunk0 = 2 * db + ((lane & 3) >> 1);
+      const int byte = 8 * (lane & 1);
+      const int r0 = tr_r, r1 = tr_r + 16;
+      const u32x2 lo = lds_read_tr16(sv + r0 * (kD * 2) + ((chunk0 ^ v_swz(r0)) << 4) + byte);
+      const u32x2 hi = lds_read_tr16(sv + r1 * (kD * 2) + ((chunk0 ^ v_swz(r1)) << 4) + byte);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
+    }
   }
-  __syncthreads();
-  for (int i = tid; i < G * kD; i += kThreads) {
-    const int hh = i / kD, dd = i % kD;
-    const float sum = red[0][hh][dd] + red[1][hh][dd] + red[2][hh][dd] + red[3][hh][dd];
-    float lsum = 0.f;
+
+  // row sum over the four 16-lane groups; normalise and write the partial
+  float lt = l + __shfl_xor(l, 16, 64);
+  lt = sum_xor32(lt);
+  if (n16 < G) {
+    const float inv = 1.f / lt;
+    float* dst = po + (long)n16 * S * kD + 4 * g4;
 #pragma unroll
-    for (int x = 0; x < G; ++x)
-      if (x == hh) lsum = l_run[x];
-    po[(long)hh * S * kD + dd] = sum / lsum;
-  }
-  if (tid < G) {
-    float mm = 0.f, ll = 1.f;
-#pragma unroll
-    for (int x = 0; x < G; ++x)
-      if (x == tid) {
-        mm = m_run[x];
-        ll = l_run[x];
-      }
-    pl[(long)tid * S] = (mm + log2_hw(ll)) * kLn2;
+    for (int db = 0; db < 8; ++db)
+      stg16(dst + 16 * db, u32x4{__float_as_uint(acc[db][0] * inv), __float_as_uint(acc[db][1] * inv),
+                                 __float_as_uint(acc[db][2] * inv), __float_as_uint(acc[db][3] * inv)});
+    if (g4 == 0) pl[(long)n16 * S] = (m + log2_hw(lt)) * kLn2;
   }
 }
 
-__global__ __launch_bounds__(kD) void decode_combine_kernel(DecodeArgs a) {
+// One workgroup per (sequence, head); wave w sums splits w, w+4, ...; every
+// lane owns 2 d values.
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float part[kCombineWaves][kD];
   const int bh = blockIdx.x;
-  const int dd = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
   const int S = a.splits;
   const float* pl = a.part_lse + (long)bh * S;
   const float* po = a.part_o + (long)bh * S * kD;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
+
+  const float lse_s = lane < S ? pl[lane] : kNegInf;
+  const float M = wave_max(lse_s);
   uint16_t* o = (uint16_t*)a.o + (long)bh * kD;
-  if (M == kNegInf) {
-    o[dd] = 0;
-    if (a.lse != nullptr && dd == 0) a.lse[bh] = kNegInf;
+  if (M == kNegInf) {  // uniform over the workgroup
+    if (tid < kD / 2) reinterpret_cast<uint32_t*>(o)[tid] = 0u;
+    if (a.lse != nullptr && tid == 0) a.lse[bh] = kNegInf;
     return;
   }
-  float wsum = 0.f, acc = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = exp2_hw((pl[s] - M) * kLog2e);
-    wsum += w;
-    acc = __builtin_fmaf(w, po[(long)s * kD + dd], acc);
+  const float w = lane < S ? exp2_hw((lse_s - M) * kLog2e) : 0.f;
+  const float W = wave_sum(w);
+  float acc0 = 0.f, acc1 = 0.f;
+  // at most 64 splits: 16 per wave, all loads independent
+#pragma unroll
+  for (int i = 0; i < 64 / kCombineWaves; ++i) {
+    const int s = wv + kCombineWaves * i;
+    const float ws = __shfl(w, s & 63, 64);
+    if (s < S) {
+      const float2 v = *reinterpret_cast<const float2*>(po + (long)s * kD + 2 * lane);
+      acc0 = __builtin_fmaf(ws, v.x, acc0);
+      acc1 = __builtin_fmaf(ws, v.y, acc1);
+    }
   }
-  const float r = acc / wsum;
-  const uint32_t packed = pack_bf16x2(r, 0.f);
-  o[dd] = (uint16_t)(packed & 0xffffu);
-  if (a.lse != nullptr && dd == 0) a.lse[bh] = M + log2_hw(wsum) * kLn2;
+  part[wv][2 * lane] = acc0;
+  part[wv][2 * lane + 1] = acc1;
+  __syncthreads();
+  if (tid < kD / 2) {
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int x = 0; x < kCombineWaves; ++x) {
+      r0 += part[x][2 * tid];
+      r1 += part[x][2 * tid + 1];
+    }
+    const float inv = 1.f / W;
+    reinterpret_cast<uint32_t*>(o)[tid] = pack_bf16x2(r0 * inv, r1 * inv);
+  }
+  if (a.lse != nullptr && tid == 0) a.lse[bh] = M + log2_hw(W) * kLn2;
 }
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, int chunk, hipStream_t stream) {
   const long grid = (long)a.B * a.Hkv * a.splits;
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, chunk);
+  hipLaunchKernelGGL(decode_split_kernel<G>, dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(kD), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(64 * kCombineWaves), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int decode_auto_splits(int B, int Hkv, int Lmax) {
-  // Chunks of about 512 keys, at most 64 splits.
-  int s = (Lmax + 511) / 512;
-  if (s < 1) s = 1;
+  // One work item per resident wave: 256 CUs x 4 SIMDs x 2 waves.  Work items
+  // that all start together and stream equal chunks finish together, so HBM
+  // stays saturated to the end; more items than slots leave a half-empty
+  // second round.  Chunks stay at least 256 keys; at most 64 splits.
+  const long pairs = (long)B * Hkv;
+  long s = pairs > 0 ? 2048 / pairs : 64;
+  const long smax = (Lmax + 255) / 256;
+  if (s > smax) s = smax;
   if (s > 64) s = 64;
-  (void)B;
-  (void)Hkv;
-  return s;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.d != kD) return hipErrorInvalidValue;
   if (a.B == 0) return hipSuccess;
   int chunk = (a.Lmax + a.splits - 1) / a.splits;
-  chunk = (chunk + 15) / 16 * 16;
-  if (chunk < 16) chunk = 16;
+  chunk = (chunk + 31) / 32 * 32;  // whole 32-key blocks
   switch (a.H / a.Hkv) {
     case 1: return launch_g<1>(a, chunk, stream);
     case 2: return launch_g<2>(a, chunk, stream);
     case 4: return launch_g<4>(a, chunk, stream);
     case 8: return launch_g<8>(a, chunk, stream);
+    case 16: return launch_g<16>(a, chunk, stream);
     default: return hipErrorInvalidValue;
   }
 }

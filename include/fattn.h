@@ -100,8 +100,11 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  *              O = 0 and LSE = -inf.
  *   o          bf16 [B, H, d]            written
  *   lse        f32  [B, H]               written, or NULL
- *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8}; d == 128; scale finite, >= 0.
- *   num_splits 0 = automatic, else 1..64.
+ *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16}; d == 128; scale finite, >= 0.
+ *   num_splits 0 = automatic (about one work item per resident wave), else 1..64: the
+ *              key range [0, Lmax) is cut into num_splits equal chunks
+ *              (rounded up to whole 32-key blocks); split s of sequence b
+ *              covers the part of chunk s below seqlens_k[b].
  *   workspace  device buffer of at least attn_decode_workspace_bytes(...)
  *              bytes for the same arguments; contents on entry are ignored.
  */

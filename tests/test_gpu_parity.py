@@ -221,7 +221,7 @@ def decode_ref(x: W.DecodeInputs, batches=None):
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3, 7, 64])
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_decode_small(splits, G):
     _need_gpu()
     Hkv = 2
