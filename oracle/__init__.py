@@ -13,6 +13,10 @@ slow and written to be read against the pages:
   four steps under "FlashAttention 的解法"; FlashAttention (TH) page, section
   "online softmax").  It exists only so that its equality with the two-pass
   form can be pinned; it is never the reference for the GPU.
+* ``attention_backward`` -- the gradients dQ, dK, dV of the forward
+  definition for a given dO (chain rule, all n x n matrices materialised);
+  the pages name the backward pass only by its memory cost (ledger page,
+  memory section).
 * ``decode`` -- one new query against all cached keys (ledger page,
   bandwidth section, the decode formula s = q^T k_j, o = sum_j p_j v_j).
 * ``hstu_jagged`` -- HSTU pointwise attention, x = QK^T, x *= alpha,
@@ -29,6 +33,8 @@ library routines.
 
 from .attention import (  # noqa: F401
     allowed_keys,
+    attention_backward,
+    attention_bwd_flops,
     attention_flops,
     attention_forward,
     attention_online,

@@ -112,6 +112,53 @@ def attention_forward(q, k, v, scale: float, causal: bool, rows=None):
     return O, L
 
 
+def attention_backward(q, k, v, do, scale: float, causal: bool):
+    """Gradients (dQ, dK, dV) of O = softmax(scale * Q K^T) V for a given dO.
+
+    q and do ``[B, H, N, d]``; k, v ``[B, Hkv, N, d]``.  Returns fp64 arrays
+    of the shapes of q, k and v.  The pages name the backward pass only by
+    its cost (ledger page, memory section: training keeps n x n backward
+    intermediates besides S and P); this is the chain rule of the forward
+    definition, written out per head with every n x n matrix materialised:
+
+        P = softmax(scale * Q K^T) (masked as in the forward)
+        dV = P^T dO
+        dP = dO V^T
+        D_i = sum_j P_ij dP_ij
+        dS = P * (dP - D)            (softmax Jacobian, row by row)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+
+    Grouped-query attention: a key/value head's gradients are the sums over
+    the query heads that read it.  A fully masked row contributes nothing.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if H % Hkv != 0:
+        raise ValueError("H must be a multiple of Hkv")
+    group = H // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            g = h // group
+            S = _mask_panel(_score_panel(q[b, h], k[b, g], scale), rows, causal)
+            P, _, _ = _softmax_two_pass(S)
+            dv[b, g] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, g].T
+            D = (P * dP).sum(axis=1)
+            dS = P * (dP - D[:, None])
+            dq[b, h] = scale * (dS @ k[b, g])
+            dk[b, g] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
 def attention_online(q, k, v, scale: float, causal: bool, block: int):
     """One-pass tiled attention with a running max and running sum (one head).
 
@@ -238,6 +285,16 @@ def attention_flops(B: int, H: int, N: int, d: int, causal: bool) -> int:
     so causal is counted as 2 n^2 d per head.
     """
     per_head = 4 * N * N * d
+    if causal:
+        per_head //= 2
+    return B * H * per_head
+
+
+def attention_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Backward FLOPs by the same convention: five products of 2 n^2 d each
+    (the score recompute QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K and
+    dK = dS^T Q), 10 n^2 d per head, halved when causal."""
+    per_head = 10 * N * N * d
     if causal:
         per_head //= 2
     return B * H * per_head
