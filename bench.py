@@ -7,14 +7,16 @@ is already resident in HBM:
   1. attn_fwd     causal prefill, B=8, H=32, N=4096, d=128, bf16  (headline)
   2. attn_decode  GQA decode, B=16, H=32, Hkv=8, L_b in [16384, 32768], d=128
   3. attn_hstu_jagged  16 jagged sequences, L_b in [512, 4096], H=4, d=64
+  4. attn_bwd     backward of step 1 (dQ, dK, dV for a synthetic dO)
 
 ``value`` is the prefill throughput in TFLOP/s with the FLOP convention of the
 ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
-prefill launch on the stream the kernel runs on; decode GB/s and HSTU TFLOP/s
-are reported beside it.  Prints ONE JSON line.
+prefill launch on the stream the kernel runs on; decode GB/s, HSTU TFLOP/s and
+backward TFLOP/s (five products, 5 n^2 d per (b, h) causal) are reported
+beside it.  Prints ONE JSON line.
 
 Other modes (used for profiling, see profiles/):
-  --only prefill|decode|hstu   run just that part of the step
+  --only prefill|decode|hstu|backward   run just that part of the step
   --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
   --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
   --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
@@ -60,7 +62,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "hstu"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward"], default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -243,17 +245,28 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
         return 0
 
-    parts = [args.only] if args.only else ["prefill", "decode", "hstu"]
+    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward"]
     print(f"bench: preparing inputs for {parts}", file=sys.stderr, flush=True)
 
     pc = W.PREFILL_D128_CAUSAL
-    px = W.dense_inputs(pc) if "prefill" in parts or not args.no_cpu_baseline else None
+    need_dense = "prefill" in parts or "backward" in parts
+    px = W.dense_inputs(pc) if need_dense or not args.no_cpu_baseline else None
     calls = {}
-    if "prefill" in parts:
+    if need_dense:
         q, k, v = bf16(px.q), bf16(px.k), bf16(px.v)
         o = torch.empty((pc.B, pc.H, pc.N, pc.d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((pc.B, pc.H, pc.N), dtype=torch.float32, device=dev)
         calls["prefill"] = lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 1)
+    if "backward" in parts:
+        from synthgen import TENSOR_DO, normal_bf16
+
+        gout = bf16(normal_bf16(pc.seed, TENSOR_DO, (pc.B, pc.H, pc.N, pc.d)))
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bwsb = fa.attn_bwd_workspace_bytes(pc.B, pc.H, pc.N)
+        bws = torch.empty(bwsb // 4, dtype=torch.float32, device=dev)
+        calls["prefill"]()  # the backward reads the forward's O and LSE
+        calls["backward"] = lambda: fa.attn_bwd(q, k, v, o, lse, gout, gq, gk, gv, pc.B, pc.H, pc.Hkv, pc.N, pc.d,
+                                                pc.scale, 1, bws, bwsb)
     dc = W.DECODE_GQA
     dx = None
     if "decode" in parts:
@@ -347,6 +360,13 @@ def main(argv=None) -> int:
                        "ms_per_call": round(ms["hstu"], 4), "flops": hf}
         if out["value"] is None:
             out.update({"value": round(ht, 2), "unit": "TFLOP/s"})
+    if "backward" in parts:
+        bf = 5 * pc.N * pc.N * pc.d * pc.B * pc.H
+        bt = bf / (ms["backward"] * 1e-3) / 1e12
+        out["backward"] = {"TFLOP/s": round(bt, 2), "frac_bf16_peak": round(bt / PEAK_BF16_TFLOPS, 4),
+                           "ms_per_call": round(ms["backward"], 4), "flops": bf}
+        if out["value"] is None:
+            out.update({"value": round(bt, 2), "unit": "TFLOP/s"})
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(px, pc, args.cpu_seconds)

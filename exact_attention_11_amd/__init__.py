@@ -23,6 +23,8 @@ __all__ = [
     "attn_decode",
     "attn_decode_workspace_bytes",
     "attn_hstu_jagged",
+    "attn_bwd",
+    "attn_bwd_workspace_bytes",
     "fattn_status_string",
     "fattn_last_error",
     "library",
@@ -39,6 +41,8 @@ EXPORTED_SYMBOLS = (
     "attn_decode_workspace_bytes",
     "attn_decode",
     "attn_hstu_jagged",
+    "attn_bwd_workspace_bytes",
+    "attn_bwd",
     "fattn_status_string",
     "fattn_last_error",
 )
@@ -76,6 +80,8 @@ _SIGNATURES = {
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "attn_hstu_jagged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _f, _i, _vp]),
+    "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "fattn_status_string": (ctypes.c_char_p, [_i]),
     "fattn_last_error": (ctypes.c_char_p, []),
 }
@@ -175,3 +181,16 @@ def attn_hstu_jagged(q, k, v, o, offsets, B, H, d, max_seqlen, alpha, inv_n, cau
     st = library().attn_hstu_jagged(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(offsets), int(B), int(H), int(d),
                                     int(max_seqlen), float(alpha), float(inv_n), int(causal), _stream(stream))
     _check("attn_hstu_jagged", st)
+
+
+def attn_bwd_workspace_bytes(B, H, N) -> int:
+    return int(library().attn_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace, workspace_bytes,
+             stream=None):
+    """Gradients of ``attn_fwd`` wrt q, k, v; see ``attn_bwd`` in include/fattn.h."""
+    st = library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                            int(B), int(H), int(Hkv), int(N), int(d), float(scale), int(causal), _ptr(workspace),
+                            int(workspace_bytes), _stream(stream))
+    _check("attn_bwd", st)

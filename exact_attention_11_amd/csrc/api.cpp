@@ -189,6 +189,52 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 1 || N < 0) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "attn_bwd";
+  int st = check_dense(fn, q, k, v, o, lse, B, H, Hkv, N, scale, causal);
+  if (st != FATTN_OK) return st;
+  if (d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (64 or 128)", fn, d);
+  if (B == 0 || N == 0) return ok();
+  if (!lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: lse, dout, dq, dk, dv and workspace must be non-null", fn);
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  // rows of one head are addressed with 32-bit byte offsets
+  if ((double)N * d * 2 >= 4294967296.0) return fail(FATTN_ERR_INVALID_ARG, "%s: N*d too large for one head", fn);
+  const size_t need = attn_bwd_workspace_bytes(B, H, N);
+  if (workspace_bytes < need)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                workspace_bytes, need);
+  fattn::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.c = std::fmax(scale * kLog2e, FLT_MIN);
+  a.causal = causal;
+  return hip_status(fattn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+}
+
 int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o, const int32_t* offsets, int B, int H,
                      int d, int max_seqlen, float alpha, float inv_n, int causal, void* stream) {
   const char* fn = "attn_hstu_jagged";

@@ -1,0 +1,481 @@
+// Attention backward on gfx950 matrix cores (bf16 in, fp32 accumulate).
+//
+// Given Q, K, V, the forward output O and its LSE, and dO, the gradients are
+// those of O = softmax(scale Q K^T) V (the chain rule of the forward
+// definition; the ledger page's memory section names the backward pass and
+// its n x n intermediates, which are never materialised here):
+//
+//   P = exp(scale Q K^T - LSE)      recomputed from the saved LSE
+//   dV = P^T dO,  dP = dO V^T,  delta_i = sum_c dO_ic O_ic
+//   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q
+//
+// Two kernels, neither uses atomics:
+//  * bwd_dq_kernel, one workgroup per 128 query rows of a (batch, head), in
+//    the forward kernel's layout: per key tile S^T = K Q^T and dP^T = V dO^T
+//    (32x32x16 products, keys on the M side), dS^T in registers, then
+//    dQ^T += K^T dS^T with K^T gathered by transposing LDS reads.  It also
+//    computes delta for its rows (from dO and O, already in registers for the
+//    fragment loads) and stores it for the second kernel.
+//  * bwd_dkdv_kernel, one workgroup per 64 keys of a (batch, kv-head), 16 keys
+//    per wave as the columns of 16x16x32 products: per step of 64 query rows
+//    (of every query head of the group) S = Q K^T and dP = dO V^T, then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T gathered by
+//    transposing reads.  The group's query heads accumulate in registers.
+// Q/dO (second kernel) and K/V (first kernel) tiles stream into LDS with
+// direct HBM->LDS loads, double buffered, one barrier per tile.  Causal tiles
+// wholly above the diagonal are skipped, straddling tiles masked per element.
+#include <cfloat>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;  // query rows per dQ workgroup (32 per wave)
+constexpr int kBN = 64;   // keys per dQ tile and per dK/dV workgroup (16 per wave)
+constexpr int kBQ = 64;   // query rows per step of the dK/dV loop
+
+// XOR on the 16-byte chunk index of row r of a K or V tile (dQ kernel).  The
+// plain operand reads (16 lanes, 16 consecutive rows, one logical chunk) and
+// the transposing reads (4 consecutive rows, 32 bytes each) both fall on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_kv(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+// Same for the Q and dO tiles of the dK/dV kernel, whose plain reads touch
+// rows 8a + 4e + b (a, b = 0..3, e fixed) of a 32-row group.
+template <int D>
+__device__ __forceinline__ int swz_q(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 3) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 3) & 3));
+}
+
+// In-block key order of the first products of the dQ kernel: swap bits 2, 3.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (relative to the 32-key block) held by accumulator element e = 4j + r of
+// a lane in half g2 (lane / 32).
+__device__ __forceinline__ int acc_key(int e, int g2) {
+  const int j = e >> 2, r = e & 3;
+  return 16 * (j >> 1) + 8 * g2 + 4 * (j & 1) + r;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) {
+  constexpr int NKB = kBN / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NDC = D / 16;
+  constexpr int ROW = D * 2;            // bytes per row
+  constexpr int TILE = kBN * ROW;       // bytes of a K or V tile
+  constexpr int NLD = TILE / 1024 / 4;  // 1 KB direct loads per wave per tile
+  static_assert(TILE % 4096 == 0, "tile split over four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TILE];  // 2 stages x (K, V)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31;
+  const int g2 = lane >> 5;
+
+  // (batch, head, query block), heaviest blocks first, all blocks of a head
+  // on one XCD (dispatch is round-robin over 8 XCDs)
+  const int G = gridDim.x;
+  int wid = blockIdx.x;
+  if ((G & 7) == 0) wid = (wid & 7) * (G >> 3) + (wid >> 3);
+  const int qb = nq - 1 - (wid % nq);
+  const int bh = wid / nq;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int g = h / (a.H / a.Hkv);
+  const int N = a.N;
+  const long qbase = ((long)b * a.H + h) * N * D;
+  const long kbase = ((long)b * a.Hkv + g) * N * D;
+  const uint16_t* qp = (const uint16_t*)a.q + qbase;
+  const uint16_t* op = (const uint16_t*)a.o + qbase;
+  const uint16_t* dop = (const uint16_t*)a.dout + qbase;
+  uint16_t* dqp = (uint16_t*)a.dq + qbase;
+  const uint16_t* kp = (const uint16_t*)a.k + kbase;
+  const uint16_t* vp = (const uint16_t*)a.v + kbase;
+
+  const int q0 = qb * kBM;
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int q0w = q0 + 32 * wv;
+  const bool wave_live = q0w < N;
+  const int qrow = q0w + n32;
+  const bool row_ok = qrow < N;
+
+  // Q and dO fragments (B operands: column n32 = row qrow, d = 16c + 8g2 ..
+  // +8) and this lane's half of delta = dO . O for the row
+  bf16x8 qf[NDC], df[NDC];
+  float dsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    u32x4 tq = {0u, 0u, 0u, 0u}, td = tq, to = tq;
+    if (row_ok) {
+      const long off = (long)qrow * D + 16 * c + 8 * g2;
+      tq = ldg16(qp + off);
+      td = ldg16(dop + off);
+      to = ldg16(op + off);
+    }
+    qf[c] = as_bf16x8(tq);
+    df[c] = as_bf16x8(td);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      dsum = __builtin_fmaf(bf16_lo(td[x]), bf16_lo(to[x]), dsum);
+      dsum = __builtin_fmaf(bf16_hi(td[x]), bf16_hi(to[x]), dsum);
+    }
+  }
+  const float delta = dsum + xor32(dsum);
+  const long rowidx = ((long)b * a.H + h) * N + qrow;
+  if (row_ok && g2 == 0) a.delta[rowidx] = delta;
+  // -LSE in base 2; rows past the end get -inf, so their weights are 0
+  const float nl = row_ok ? -a.lse[rowidx] * kLog2e : kNegInf;
+  const float c2 = a.c;
+
+  // K/V tile loads: wave instruction i fills LDS bytes (wv + 4i) KB .. +1 KB
+  // of a tile; the swizzle is applied through the source address
+  uint32_t toff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int byte = (wv + 4 * i) * 1024 + 16 * lane;
+    const int r = byte / ROW;
+    const int pc = (byte % ROW) / 16;
+    toff[i] = (uint32_t)r * ROW + (uint32_t)(pc ^ swz_kv<D>(r)) * 16u;
+  }
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto load_tile = [&](int j) {
+    const int k0 = j * kBN;
+    const uint32_t bytes = (uint32_t)(N - k0) * ROW;  // rows k0 .. N-1
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * D, bytes);
+    const uint32_t st = lds0 + (uint32_t)(j & 1) * 2 * TILE + wv * 1024;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rk, st + 4096 * i, toff[i]);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rv, st + TILE + 4096 * i, toff[i]);
+  };
+
+  // transposing reads of K^T: row offset within the 8-key group and (chunk,
+  // byte) of the 4 d values this lane addresses
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  load_tile(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem();      // this wave's pieces of tile j have landed
+    __syncthreads();  // everyone's have; stage (j+1)&1 is free
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const int k0 = j * kBN;
+    const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
+    if (!active) continue;
+    const unsigned char* sk = smem + (j & 1) * 2 * TILE;
+    const unsigned char* sv = sk + TILE;
+
+    // S^T = K Q^T and dP^T = V dO^T (keys on the M side, in key_perm order)
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int r = 32 * kb + key_perm(n32);
+        const int off = r * ROW + (((2 * c + g2) ^ swz_kv<D>(r)) << 4);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + off);
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + off);
+        const f32x16 zero = {};
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), df[c], c == 0 ? zero : dp[kb], 0, 0, 0);
+      }
+    }
+    if ((CAUSAL && k0 + kBN - 1 > q0w) || (k0 + kBN > N)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kb + acc_key(e, g2);
+          if (!(key < N && (!CAUSAL || key <= qrow))) s[kb][e] = kNegInf;
+        }
+    }
+    // dS^T = P^T (dP^T - delta) as bf16 pairs (B operand of the next product)
+    uint32_t pk[NKB][8];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_hw(__builtin_fmaf(s[kb][e], c2, nl));
+        x[e] = p * (dp[kb][e] - delta);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    }
+    // dQ^T += K^T dS^T; K^T fragments gathered by transposing reads
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
+        const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int ch = 4 * db + tr_chunk;
+          const u32x2 lo = lds_read_tr16(sk + krow * ROW + ((ch ^ swz_kv<D>(krow)) << 4) + tr_byte);
+          const u32x2 hi = lds_read_tr16(sk + (krow + 4) * ROW + ((ch ^ swz_kv<D>(krow + 4)) << 4) + tr_byte);
+          const u32x4 kt = {lo[0], lo[1], hi[0], hi[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt), as_bf16x8(pw), acc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const float sc = a.scale;
+  uint16_t* drow = dqp + (long)qrow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      u32x2 t;
+      t[0] = pack_bf16x2(acc[db][4 * jq] * sc, acc[db][4 * jq + 1] * sc);
+      t[1] = pack_bf16x2(acc[db][4 * jq + 2] * sc, acc[db][4 * jq + 3] * sc);
+      stg8(drow + 32 * db + 8 * jq + 4 * g2, t);
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+  constexpr int ROW = D * 2;
+  constexpr int QT = kBQ * ROW;         // bytes of a Q or dO tile
+  constexpr int SLOT = 2 * QT + 2048;   // Q, dO, LSE (1 KB), delta (1 KB)
+  constexpr int NLD = QT / 1024 / 4;    // 1 KB direct loads per wave per tile
+  constexpr int NDS = D / 32;           // k-steps over d of the 16x16x32 products
+  constexpr int NDB = D / 16;           // 16-row blocks of d in the accumulators
+  static_assert(QT % 4096 == 0, "tile split over four waves");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  // (batch, kv-head, key block); the first key blocks carry the most causal
+  // work and go first; all blocks of a kv-head on one XCD
+  const int Gd = gridDim.x;
+  int wid = blockIdx.x;
+  if ((Gd & 7) == 0) wid = (wid & 7) * (Gd >> 3) + (wid >> 3);
+  const int kblk = wid % nkb;
+  const int bg = wid / nkb;
+  const int g = bg % a.Hkv;
+  const int b = bg / a.Hkv;
+  const int N = a.N;
+  const int grp = a.H / a.Hkv;
+  const int k0 = kblk * kBN;
+  const int kw0 = k0 + 16 * wv;  // this wave's first key
+  const int key = kw0 + l16;     // this lane's key (column of the products)
+  const bool key_ok = key < N;
+  const long kbase = ((long)b * a.Hkv + g) * N * D;
+
+  // K^T and V^T fragments (B operands): column = key, k = d 32s + 8g4 .. +8
+  bf16x8 kf[NDS], vf[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    u32x4 tk = {0u, 0u, 0u, 0u}, tv = tk;
+    if (key_ok) {
+      const long off = kbase + (long)key * D + 32 * s + 8 * g4;
+      tk = ldg16((const uint16_t*)a.k + off);
+      tv = ldg16((const uint16_t*)a.v + off);
+    }
+    kf[s] = as_bf16x8(tk);
+    vf[s] = as_bf16x8(tv);
+  }
+
+  f32x4 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nqb = (N + kBQ - 1) / kBQ;
+  const int i0 = CAUSAL ? kblk : 0;  // kBQ == kBN: query block kblk holds the diagonal
+  const int per_head = nqb - i0;
+  const int steps = grp * per_head;
+
+  // Q/dO tile loads: wave instruction i fills LDS bytes (wv + 4i) KB .. +1 KB
+  uint32_t toff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int byte = (wv + 4 * i) * 1024 + 16 * lane;
+    const int r = byte / ROW;
+    const int pc = (byte % ROW) / 16;
+    toff[i] = (uint32_t)r * ROW + (uint32_t)(pc ^ swz_q<D>(r)) * 16u;
+  }
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto load_step = [&](int t) {
+    const int hh = t / per_head;
+    const int r0 = (i0 + t % per_head) * kBQ;
+    const long rowbase = ((long)b * a.H + g * grp + hh) * N + r0;
+    const uint32_t bytes = (uint32_t)(N - r0) * ROW;  // rows r0 .. N-1
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + rowbase * D, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const uint16_t*)a.dout + rowbase * D, bytes);
+    const uint32_t st = lds0 + (uint32_t)(t & 1) * SLOT;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rq, st + (wv + 4 * i) * 1024, toff[i]);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) lds_dma16(rd, st + QT + (wv + 4 * i) * 1024, toff[i]);
+    // LSE and delta of rows r0 .. r0+63 (1 KB of LDS each; lanes past the 64
+    // values land in the unused rest of the region)
+    if (wv == 0) lds_dma16(make_rsrc(a.lse + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT, 16u * lane);
+    if (wv == 1) lds_dma16(make_rsrc(a.delta + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT + 1024, 16u * lane);
+  };
+
+  const float c2 = a.c;
+  load_step(0);
+  for (int t = 0; t < steps; ++t) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < steps) load_step(t + 1);
+    const int r0 = (i0 + t % per_head) * kBQ;
+    const unsigned char* sq = smem + (t & 1) * SLOT;
+    const unsigned char* sdo = sq + QT;
+    const float* sl = reinterpret_cast<const float*>(sq + 2 * QT);
+    const float* sd = sl + 256;
+
+    // row values of this lane: rows r0 + 32 t2 + 8 g4 + 4e + r
+    float nl[2][8], dl[2][8];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl + 32 * t2 + 8 * g4);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(sl + 32 * t2 + 8 * g4 + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(sd + 32 * t2 + 8 * g4);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(sd + 32 * t2 + 8 * g4 + 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        nl[t2][r] = -l0[r] * kLog2e;
+        nl[t2][4 + r] = -l1[r] * kLog2e;
+        dl[t2][r] = d0[r];
+        dl[t2][4 + r] = d1[r];
+      }
+    }
+
+    // S = Q K^T and dP = dO V^T: row block rb = 2 t2 + e holds, in accumulator
+    // row 4 g + r, query 32 t2 + 8 g + 4e + r, so each lane's 8 values of a
+    // 32-query step are 8 consecutive queries (the B operand of the next
+    // products); the A operand rows are read in that permuted order
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int qr = 32 * (rb >> 1) + 8 * (l16 >> 2) + 4 * (rb & 1) + (l16 & 3);
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int off = qr * ROW + (((4 * ds + g4) ^ swz_q<D>(qr)) << 4);
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(sq + off);
+        const u32x4 ad = *reinterpret_cast<const u32x4*>(sdo + off);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aq), kf[ds], ds == 0 ? zero : s[rb], 0, 0, 0);
+        dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ad), vf[ds], ds == 0 ? zero : dp[rb], 0, 0, 0);
+      }
+    }
+    if ((CAUSAL && r0 < kw0 + 15) || (r0 + kBQ > N) || (kw0 + 16 > N)) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + 32 * (rb >> 1) + 8 * g4 + 4 * (rb & 1) + r;
+          if (!(key_ok && row < N && (!CAUSAL || key <= row))) s[rb][r] = kNegInf;
+        }
+    }
+    // P and dS as bf16 pairs: step t2, dwords 2e and 2e+1 = queries 8g4 + 4e + 0..3
+    uint32_t pw[2][4], sw[2][4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float p[4], x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = exp2_hw(__builtin_fmaf(s[2 * t2 + e][r], c2, nl[t2][4 * e + r]));
+          x[r] = p[r] * (dp[2 * t2 + e][r] - dl[t2][4 * e + r]);
+        }
+        pw[t2][2 * e] = pack_bf16x2(p[0], p[1]);
+        pw[t2][2 * e + 1] = pack_bf16x2(p[2], p[3]);
+        sw[t2][2 * e] = pack_bf16x2(x[0], x[1]);
+        sw[t2][2 * e + 1] = pack_bf16x2(x[2], x[3]);
+      }
+
+    // dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T by transposing reads:
+    // lane l16 of group g4 gets d = 16 db + l16 for queries 32 t2 + 8 g4 + 0..7
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 pv = {pw[t2][0], pw[t2][1], pw[t2][2], pw[t2][3]};
+      const u32x4 sv = {sw[t2][0], sw[t2][1], sw[t2][2], sw[t2][3]};
+      const int ra = 32 * t2 + 8 * g4 + (l16 >> 2);
+      const int rc = ra + 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int ch = 2 * db + ((l16 & 3) >> 1);
+        const int oa = ra * ROW + ((ch ^ swz_q<D>(ra)) << 4) + 8 * (l16 & 1);
+        const int oc = rc * ROW + ((ch ^ swz_q<D>(rc)) << 4) + 8 * (l16 & 1);
+        const u32x2 dlo = lds_read_tr16(sdo + oa);
+        const u32x2 dhi = lds_read_tr16(sdo + oc);
+        const u32x2 qlo = lds_read_tr16(sq + oa);
+        const u32x2 qhi = lds_read_tr16(sq + oc);
+        const u32x4 dt = {dlo[0], dlo[1], dhi[0], dhi[1]};
+        const u32x4 qt = {qlo[0], qlo[1], qhi[0], qhi[1]};
+        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dt), as_bf16x8(pv), dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qt), as_bf16x8(sv), dk[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!key_ok) return;
+  // accumulator row 4 g4 + r of block db is d = 16 db + 4 g4 + r of this key
+  const float sc = a.scale;
+  uint16_t* dkrow = (uint16_t*)a.dk + kbase + (long)key * D;
+  uint16_t* dvrow = (uint16_t*)a.dv + kbase + (long)key * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    u32x2 tk, tv;
+    tk[0] = pack_bf16x2(dk[db][0] * sc, dk[db][1] * sc);
+    tk[1] = pack_bf16x2(dk[db][2] * sc, dk[db][3] * sc);
+    tv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
+    tv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
+    stg8(dkrow + 16 * db + 4 * g4, tk);
+    stg8(dvrow + 16 * db + 4 * g4, tv);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t stream) {
+  const int nq = (a.N + kBM - 1) / kBM;
+  const long g1 = (long)nq * a.H * a.B;
+  const int nkb = (a.N + kBN - 1) / kBN;
+  const long g2 = (long)nkb * a.Hkv * a.B;
+  if (g1 <= 0) return hipSuccess;
+  if (g1 > 0x7fffffffL || g2 > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a, nq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a, nkb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch_bwd_one<128, true>(a, stream) : launch_bwd_one<128, false>(a, stream);
+  if (a.d == 64) return a.causal ? launch_bwd_one<64, true>(a, stream) : launch_bwd_one<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fattn

@@ -58,6 +58,34 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
+// Direct HBM -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i's bytes from byte offset `off` land at LDS byte lds_addr + 16*i
+// (lds_addr the same in every lane of the wave); out-of-range lanes write
+// zeros.  Written as inline assembly on purpose: the compiler then does not
+// model the load's LDS write, so it inserts no vmcnt(0) drain in front of
+// later LDS reads it cannot prove disjoint (it cannot for the transposing
+// reads).  The caller orders the data with wait_vmem and a barrier.  The
+// instruction writes no VGPR; m0 (the LDS base) is saved and restored.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t off) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(off), "s"(r)
+      : "memory");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Wait until this wave's outstanding vector-memory operations (including the
+// direct-to-LDS loads) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,

@@ -64,4 +64,25 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Automatic split count for a decode shape.
 int decode_auto_splits(int B, int Hkv, int Lmax);
 
+struct BwdArgs {
+  const void* q;      // [B, H, N, d] bf16
+  const void* k;      // [B, Hkv, N, d] bf16
+  const void* v;
+  const void* o;      // forward output [B, H, N, d] bf16
+  const float* lse;   // forward LSE [B, H, N] (natural log)
+  const void* dout;   // dO [B, H, N, d] bf16
+  void* dq;           // [B, H, N, d] bf16
+  void* dk;           // [B, Hkv, N, d] bf16
+  void* dv;
+  float* delta;       // workspace [B, H, N]: rowsum(dO * O)
+  int B, H, Hkv, N, d;
+  float scale;        // softmax scale
+  float c;            // scale * log2(e), clamped to >= FLT_MIN
+  int causal;
+};
+
+// Attention backward: dQ (and the row sums delta) by query blocks, then dK, dV
+// by key blocks.
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
 }  // namespace fattn

@@ -138,6 +138,43 @@ int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o,
                      const int32_t* offsets, int B, int H, int d, int max_seqlen,
                      float alpha, float inv_n, int causal, void* stream);
 
+/*
+ * attn_bwd_workspace_bytes -- device workspace attn_bwd needs: one f32 per
+ * query row (the row sums delta below), rounded up to 256 bytes.  Returns 0
+ * for an invalid shape.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * attn_bwd -- gradients of attn_fwd with respect to q, k and v.
+ *
+ * The pages name the backward pass only by its cost (ledger page, memory
+ * section: training keeps n x n backward intermediates besides S and P);
+ * this entry point computes it without them.  With P = exp(scale Q K^T -
+ * LSE) recomputed from the forward's LSE (masked as in the forward):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  delta_i = sum_c dO_ic O_ic,
+ *   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,
+ *
+ * and for grouped-query attention a key/value head's gradients sum over
+ * the query heads that read it.
+ *
+ *   q, o, dout   bf16 [B, H,   N, d]  (o and lse as written by attn_fwd
+ *                                      with the same arguments)
+ *   k, v         bf16 [B, Hkv, N, d]
+ *   lse          f32  [B, H,   N]     natural log, as from attn_fwd
+ *   dq           bf16 [B, H,   N, d]  written
+ *   dk, dv       bf16 [B, Hkv, N, d]  written
+ *   workspace    device buffer of at least attn_bwd_workspace_bytes(B, H, N)
+ *                bytes; contents on entry are ignored (it receives delta).
+ *   H % Hkv == 0; d in {64, 128}; scale finite and >= 0; causal in {0, 1}.
+ *   B == 0 or N == 0 is a valid empty call.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fattn_status_string(int status);
 

@@ -33,6 +33,7 @@ TENSOR_Q = 1
 TENSOR_K = 2
 TENSOR_V = 3
 TENSOR_LENGTHS = 4
+TENSOR_DO = 5  # upstream gradient dO of the backward pass
 
 
 def _rng(seed: int, tensor_id: int) -> np.random.Generator:

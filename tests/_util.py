@@ -19,6 +19,11 @@ BF16_REL_MAX = 2e-2
 F32_MAX_ABS = 1e-5
 F32_REL_FRO = 1e-6
 LSE_MAX_ABS = 1e-3
+# Gradients (backward pass): their scale grows with N and the scores, so the
+# bound is relative -- Frobenius error and max error, both normalised by the
+# reference.  bf16 rounding of P, dS and the outputs gives about 2^-9 per term.
+GRAD_REL_FRO = 1e-2
+GRAD_REL_MAX = 2e-2
 
 
 def to_dev_bf16(bits: np.ndarray):
@@ -92,6 +97,12 @@ def lse_ok(got, ref) -> tuple[bool, Diff]:
 def assert_bf16(got, ref, what=""):
     ok, r = bf16_ok(got, ref)
     assert ok, f"{what}: {r}"
+    return r
+
+
+def assert_grad(got, ref, what=""):
+    r = diff(got, ref)
+    assert r.finite and r.rel_fro <= GRAD_REL_FRO and r.rel_max <= GRAD_REL_MAX, f"{what}: {r}"
     return r
 
 

@@ -156,6 +156,43 @@ def test_hstu_empty_calls_launch_nothing():
     _hstu(q=0, k=0, v=0, o=0, offsets=0, max_seqlen=0)
 
 
+def _bwd(**kw):
+    B, H, Hkv, N, d = 2, 4, 2, 100, 128
+    ws = fa.attn_bwd_workspace_bytes(B, H, N)
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=B, H=H, Hkv=Hkv, N=N, d=d, scale=0.1,
+                causal=1, workspace=P, workspace_bytes=ws)
+    args.update(kw)
+    fa.attn_bwd(stream=S0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(dk=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(workspace_bytes=256), fa.FATTN_ERR_INVALID_ARG),
+    (dict(dq=P + 4), fa.FATTN_ERR_INVALID_ARG),
+    (dict(H=3), fa.FATTN_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FATTN_ERR_INVALID_ARG),
+    (dict(d=96), fa.FATTN_ERR_UNSUPPORTED),
+])
+def test_attn_bwd_rejects(kw, status):
+    with pytest.raises(fa.FattnError) as e:
+        _bwd(**kw)
+    assert e.value.status == status
+    assert fa.fattn_last_error().startswith("attn_bwd")
+
+
+def test_bwd_workspace_size_and_empty_calls():
+    # one f32 per query row, rounded to 256 B
+    assert fa.attn_bwd_workspace_bytes(2, 4, 100) == 3328
+    assert fa.attn_bwd_workspace_bytes(8, 32, 4096) == 8 * 32 * 4096 * 4
+    assert fa.attn_bwd_workspace_bytes(1, 0, 10) == 0
+    _bwd(q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, workspace=0, B=0)
+    _bwd(q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, workspace=0, N=0)
+
+
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_lib", None)
     monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "libfattn.so"))
