@@ -19,6 +19,9 @@ slow and written to be read against the pages:
   memory section).
 * ``decode`` -- one new query against all cached keys (ledger page,
   bandwidth section, the decode formula s = q^T k_j, o = sum_j p_j v_j).
+* ``decode_paged`` -- ``decode`` over a paged cache: the pages of each
+  sequence gathered in logical order through its block table (the
+  PagedAttention scheme named on the CANN ops-transformer FlashAttention page).
 * ``hstu_jagged`` -- HSTU pointwise attention, x = QK^T, x *= alpha,
   x = silu(x), x *= mask / n, O = x V (HSTU page, the Python listing under
   "先搞懂：HSTU到底难在哪"), over packed variable-length sequences
@@ -40,6 +43,7 @@ from .attention import (  # noqa: F401
     attention_online,
     attention_probs,
     decode,
+    decode_paged,
     hstu_dense,
     hstu_flops,
     hstu_jagged,

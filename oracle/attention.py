@@ -216,6 +216,9 @@ def decode(q, k_cache, v_cache, seqlens, scale: float):
     L = np.zeros((B, H))
     for b in range(B):
         n = int(seqlens[b])
+        if n == 0:  # empty history: no visible key, O = 0 and LSE = -inf
+            L[b] = -np.inf
+            continue
         for h in range(H):
             g = h // group
             kk = np.asarray(k_cache[b, g, :n], dtype=np.float64)
@@ -225,6 +228,39 @@ def decode(q, k_cache, v_cache, seqlens, scale: float):
             O[b, h] = (P @ vv)[0]
             with np.errstate(divide="ignore"):
                 L[b, h] = m[0] + np.log(l[0])
+    return O, L
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale: float):
+    """Decode over a paged cache: gather each sequence's pages in logical order,
+    then ``decode``.
+
+    q ``[B, H, d]``; pages ``[num_pages, Hkv, P, d]``; block_table
+    ``[B, max_pages]`` (logical page p of sequence b is physical page
+    ``block_table[b, p]``); seqlens ``[B]``.
+
+    The paged cache is the PagedAttention scheme that the CANN ops-transformer
+    FlashAttention page names under KV-cache management (Kwon et al. 2023 in
+    the FlashAttention (TH) page's bibliography); paging changes where keys
+    live, not what attention computes, so the result is plain decode on the
+    gathered rows [0, L_b).  Pages past the last one holding a valid row are
+    not read.
+    """
+    B, H, d = np.asarray(q).shape
+    P = k_pages.shape[2]
+    O = np.zeros((B, H, v_pages.shape[3]))
+    L = np.zeros((B, H))
+    for b in range(B):
+        n = int(seqlens[b])
+        used = block_table[b, :(n + P - 1) // P]
+        # [pages, Hkv, P, d] -> [Hkv, pages * P, d], rows in logical order
+        if n == 0:  # empty history, as in decode
+            L[b] = -np.inf
+            continue
+        kb = np.concatenate([k_pages[p] for p in used], axis=1)
+        vb = np.concatenate([v_pages[p] for p in used], axis=1)
+        Ob, Lb = decode(np.asarray(q)[b:b + 1], kb[None, :, :n], vb[None, :, :n], np.array([n]), scale)
+        O[b], L[b] = Ob[0], Lb[0]
     return O, L
 
 

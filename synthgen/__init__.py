@@ -34,6 +34,7 @@ TENSOR_K = 2
 TENSOR_V = 3
 TENSOR_LENGTHS = 4
 TENSOR_DO = 5  # upstream gradient dO of the backward pass
+TENSOR_PAGES = 6  # physical page order of a paged KV cache
 
 
 def _rng(seed: int, tensor_id: int) -> np.random.Generator:

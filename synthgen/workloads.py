@@ -34,6 +34,7 @@ import numpy as np
 from . import (
     BF16_QNAN,
     TENSOR_K,
+    TENSOR_PAGES,
     TENSOR_Q,
     TENSOR_V,
     bf16_bits_to_f64,
@@ -142,6 +143,41 @@ def decode_inputs(c: Decode, seqlens=None) -> DecodeInputs:
         k[b, :, seqlens[b]:, :] = BF16_QNAN
         v[b, :, seqlens[b]:, :] = BF16_QNAN
     return DecodeInputs(c, q, k, v, seqlens)
+
+
+@dataclass
+class PagedDecodeInputs:
+    base: DecodeInputs       # the same cache, contiguous
+    page_size: int
+    k_pages: np.ndarray      # bf16 bits [num_pages, Hkv, page_size, d]
+    v_pages: np.ndarray
+    block_table: np.ndarray  # int32 [B, max_pages]
+    num_pages: int
+
+
+def paged_from_decode(x: DecodeInputs, page_size: int, spare_pages: int = 64, perm_seed: int = 0
+                      ) -> PagedDecodeInputs:
+    """Scatter a contiguous decode cache into pages of ``page_size`` rows, in a
+    seeded random physical order.  Spare pages (never referenced) and rows past
+    Lmax are NaN, so a wrong page or row read shows up in the output."""
+    c = x.case
+    P = int(page_size)
+    ppseq = (c.Lmax + P - 1) // P
+    num_pages = c.B * ppseq + spare_pages
+    rng = np.random.default_rng(np.random.SeedSequence([c.seed, TENSOR_PAGES, perm_seed]))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = perm[:c.B * ppseq].reshape(c.B, ppseq)
+
+    def scatter(cache):
+        pad = ppseq * P - c.Lmax
+        if pad:
+            cache = np.concatenate([cache, np.full(cache.shape[:2] + (pad, c.d), BF16_QNAN, np.uint16)], axis=2)
+        pages = np.full((num_pages, c.Hkv, P, c.d), BF16_QNAN, dtype=np.uint16)
+        pages[table.reshape(-1)] = (cache.reshape(c.B, c.Hkv, ppseq, P, c.d).transpose(0, 2, 1, 3, 4)
+                                    .reshape(c.B * ppseq, c.Hkv, P, c.d))
+        return pages
+
+    return PagedDecodeInputs(x, P, scatter(x.k), scatter(x.v), table, num_pages)
 
 
 @dataclass
