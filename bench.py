@@ -8,6 +8,7 @@ is already resident in HBM:
   2. attn_decode  GQA decode, B=16, H=32, Hkv=8, L_b in [16384, 32768], d=128
   3. attn_hstu_jagged  16 jagged sequences, L_b in [512, 4096], H=4, d=64
   4. attn_bwd     backward of step 1 (dQ, dK, dV for a synthetic dO)
+  5. attn_decode_paged  step 2's cache in pages of 16 rows, shuffled
 
 ``value`` is the prefill throughput in TFLOP/s with the FLOP convention of the
 ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
@@ -16,7 +17,7 @@ backward TFLOP/s (five products, 5 n^2 d per (b, h) causal) are reported
 beside it.  Prints ONE JSON line.
 
 Other modes (used for profiling, see profiles/):
-  --only prefill|decode|hstu|backward   run just that part of the step
+  --only prefill|decode|hstu|backward|decode_paged   run just that part of the step
   --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
   --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
   --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
@@ -62,7 +63,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged"], default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -245,7 +246,7 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
         return 0
 
-    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward"]
+    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward", "decode_paged"]
     print(f"bench: preparing inputs for {parts}", file=sys.stderr, flush=True)
 
     pc = W.PREFILL_D128_CAUSAL
@@ -269,8 +270,25 @@ def main(argv=None) -> int:
                                                 pc.scale, 1, bws, bwsb)
     dc = W.DECODE_GQA
     dx = None
-    if "decode" in parts:
+    if "decode" in parts or "decode_paged" in parts:
         dx = W.decode_inputs(dc)
+    if "decode_paged" in parts:
+        page = 16
+        pdx = W.paged_from_decode(dx, page)
+        pq, pk, pv = bf16(dx.q), bf16(pdx.k_pages), bf16(pdx.v_pages)
+        ptab = torch.from_numpy(pdx.block_table).to(dev)
+        psl = torch.from_numpy(dx.seqlens).to(dev)
+        pmp = pdx.block_table.shape[1]
+        pnp = pdx.num_pages
+        po = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device=dev)
+        plse = torch.empty((dc.B, dc.H), dtype=torch.float32, device=dev)
+        pwsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, pmp * page, dc.d, args.splits)
+        pws = torch.empty(pwsb // 4, dtype=torch.float32, device=dev)
+        calls["decode_paged"] = lambda: fa.attn_decode_paged(pq, pk, pv, ptab, psl, po, plse, dc.B, dc.H, dc.Hkv, page,
+                                                             pmp, pnp, dc.d, dc.scale, args.splits, pws,
+                                                             pwsb)
+        del pdx
+    if "decode" in parts:
         dq, dk, dv = bf16(dx.q), bf16(dx.k), bf16(dx.v)
         dsl = torch.from_numpy(dx.seqlens).to(dev)
         do = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device=dev)
@@ -351,6 +369,17 @@ def main(argv=None) -> int:
         out["decode"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "ms_per_call": round(ms["decode"], 4), "algorithmic_bytes": nbytes, "sum_L": ssum,
                          "splits": args.splits or "auto"}
+        if out["value"] is None:
+            out.update({"value": round(gbs, 1), "unit": "GB/s"})
+    if "decode_paged" in parts:
+        ssum = int(dx.seqlens.sum())
+        # same algorithmic bytes as the contiguous decode (the block-table reads,
+        # 4 bytes per 16-row page, are under 0.01 % and not counted)
+        nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
+        gbs = nbytes / (ms["decode_paged"] * 1e-3) / 1e9
+        out["decode_paged"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                               "ms_per_call": round(ms["decode_paged"], 4), "algorithmic_bytes": nbytes,
+                               "page_size": 16, "splits": args.splits or "auto"}
         if out["value"] is None:
             out.update({"value": round(gbs, 1), "unit": "GB/s"})
     if "hstu" in parts:

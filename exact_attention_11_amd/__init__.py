@@ -22,6 +22,7 @@ __all__ = [
     "attn_fwd_f32",
     "attn_decode",
     "attn_decode_workspace_bytes",
+    "attn_decode_paged",
     "attn_hstu_jagged",
     "attn_bwd",
     "attn_bwd_workspace_bytes",
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "attn_fwd_f32",
     "attn_decode_workspace_bytes",
     "attn_decode",
+    "attn_decode_paged",
     "attn_hstu_jagged",
     "attn_bwd_workspace_bytes",
     "attn_bwd",
@@ -79,6 +81,8 @@ _SIGNATURES = {
     "attn_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                               _vp]),
     "attn_hstu_jagged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _f, _i, _vp]),
     "attn_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
@@ -174,6 +178,16 @@ def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scal
                                int(B), int(H), int(Hkv), int(Lmax), int(d), float(scale), int(num_splits),
                                _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("attn_decode", st)
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, o, lse, B, H, Hkv, page_size, max_pages_per_seq,
+                      num_pages, d, scale, num_splits, workspace, workspace_bytes, stream=None):
+    """Split-KV decode over a paged cache; see ``attn_decode_paged`` in include/fattn.h."""
+    st = library().attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens_k),
+                                     _ptr(o), _ptr(lse), int(B), int(H), int(Hkv), int(page_size),
+                                     int(max_pages_per_seq), int(num_pages), int(d), float(scale), int(num_splits),
+                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("attn_decode_paged", st)
 
 
 def attn_hstu_jagged(q, k, v, o, offsets, B, H, d, max_seqlen, alpha, inv_n, causal, stream=None):

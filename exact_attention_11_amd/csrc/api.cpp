@@ -189,6 +189,72 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
 }
 
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Hkv, int page_size,
+                      int max_pages_per_seq, int num_pages, int d, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const char* fn = "attn_decode_paged";
+  if (B < 0) return fail(FATTN_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+  if (H < 1 || Hkv < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: H and Hkv must be >= 1", fn);
+  if (H % Hkv != 0) return fail(FATTN_ERR_INVALID_ARG, "%s: H=%d is not a multiple of Hkv=%d", fn, H, Hkv);
+  if (page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: page_size must be a power of two in [16, 1024] (got %d)", fn,
+                page_size);
+  if (max_pages_per_seq < 1 || num_pages < 1)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: max_pages_per_seq and num_pages must be >= 1", fn);
+  if ((double)max_pages_per_seq * page_size > 2147483647.0)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: max_pages_per_seq*page_size too large", fn);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: scale must be finite and >= 0 (got %g)", fn, (double)scale);
+  if (num_splits < 0 || num_splits > 64)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: num_splits must be 0 (auto) or 1..64 (got %d)", fn, num_splits);
+  const int G = H / Hkv;
+  if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8 or 16)", fn, G);
+  if (B == 0) return ok();
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !o || !workspace)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: q, pages, block_table, seqlens_k, o and workspace must be non-null",
+                fn);
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(workspace) ||
+      (lse && !aligned16(lse)))
+    return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  const int Lmax = max_pages_per_seq * page_size;
+  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax) : num_splits;
+  int chunk = (Lmax + splits - 1) / splits;
+  chunk = (chunk + 31) / 32 * 32;
+  if ((chunk + page_size - 1) / page_size > fattn::kDecodeMaxSplitPages)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: one split would span %d pages (at most %d); use more splits or larger pages",
+                fn, (chunk + page_size - 1) / page_size, fattn::kDecodeMaxSplitPages);
+  const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
+  if (workspace_bytes < need)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                workspace_bytes, need);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  fattn::DecodeArgs a{};
+  a.q = q;
+  a.k = k_pages;
+  a.v = v_pages;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Lmax = Lmax;
+  a.d = d;
+  a.c = scale * kLog2e;
+  a.splits = splits;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)B * H * splits * d;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.page_shift = shift;
+  a.num_pages = num_pages;
+  return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_paged launch");
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 1 || N < 0) return 0;
   const size_t bytes = (size_t)B * H * N * sizeof(float);

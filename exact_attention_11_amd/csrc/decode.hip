@@ -55,9 +55,11 @@ __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | (((r >> 2)
 //   online softmax per column on the accumulator (8 scores per lane)
 //   O^T[128 d x 16 cols] += V^T P^T   (8 steps; V^T from LDS by transposing
 //                                      reads, P^T straight from the scores)
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chunk) {
   __shared__ __attribute__((aligned(16))) unsigned char sv[32 * kD * 2];
+  // paged cache: physical page of each logical page this split touches
+  __shared__ int pt[PAGED ? kDecodeMaxSplitPages + 2 : 1];
   const int lane = threadIdx.x;
   const int n16 = lane & 15;  // column (query head) of the 16x16 tiles
   const int g4 = lane >> 4;   // 16-lane group
@@ -87,9 +89,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
   // rows [kb0, kb1) of this kv-head; loads past kb1 read zero
   const long rowbase = ((long)b * a.Hkv + g) * a.Lmax + kb0;
   const uint32_t bytes = (uint32_t)(kb1 - kb0) * (kD * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + rowbase * kD, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + rowbase * kD, bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + (PAGED ? 0 : rowbase * kD), bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + (PAGED ? 0 : rowbase * kD), bytes);
   const int n = kb1 - kb0;
+
+  // paged cache: stage the block-table entries of pages lp0 .. (kb1-1)/P, plus
+  // one (the half block just past the chunk end), clamped to valid pages
+  const int sh = a.page_shift;
+  const int lp0 = kb0 >> sh;
+  if constexpr (PAGED) {
+    const int np = ((kb1 - 1) >> sh) - lp0 + 2;
+    const int32_t* tb = a.block_table + (long)b * a.max_pages;
+    for (int i = lane; i < np; i += 64) {
+      const int lp = lp0 + i;
+      int pg = lp < a.max_pages ? tb[lp] : 0;
+      pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+      pt[i] = pg;
+    }
+  }
 
   // Q^T operand: column n16 = head h0 + n16 (zero for n16 >= G), d = 32c + 8*g4 .. +8
   bf16x8 qf[4];
@@ -116,14 +133,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
 
   u32x4 kr[8], vr[8];
   auto issue = [&](int blk) {
-    const uint32_t o = (uint32_t)blk * (kD * 2);
+    if constexpr (PAGED) {
+      // rows 0-15 and 16-31 of the block each lie within one page (pages
+      // hold a power of two >= 16 keys, blocks start at multiples of 32)
+      const int t = kb0 + blk;
+      const int pA = __builtin_amdgcn_readfirstlane(pt[(t >> sh) - lp0]);
+      const int pB = __builtin_amdgcn_readfirstlane(pt[((t + 16) >> sh) - lp0]);
+      const int m = (1 << sh) - 1;
+      const long rowA = (((long)pA * a.Hkv + g) << sh) + (t & m);
+      const long rowB = (((long)pB * a.Hkv + g) << sh) + ((t + 16) & m);
+      const uint32_t nA = (uint32_t)min(16, kb1 - t) * (kD * 2);
+      const uint32_t nB = (uint32_t)max(0, min(16, kb1 - t - 16)) * (kD * 2);
+      const __amdgpu_buffer_rsrc_t kA = make_rsrc((const uint16_t*)a.k + rowA * kD, nA);
+      const __amdgpu_buffer_rsrc_t kB = make_rsrc((const uint16_t*)a.k + rowB * kD, nB);
+      const __amdgpu_buffer_rsrc_t vA = make_rsrc((const uint16_t*)a.v + rowA * kD, nA);
+      const __amdgpu_buffer_rsrc_t vB = make_rsrc((const uint16_t*)a.v + rowB * kD, nB);
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      kr[c2] = buf_load16(rk, o + koff + 64u * c2);
-      kr[4 + c2] = buf_load16(rk, o + 16u * (kD * 2) + koff + 64u * c2);
+      for (int c2 = 0; c2 < 4; ++c2) {
+        kr[c2] = buf_load16(kA, koff + 64u * c2);
+        kr[4 + c2] = buf_load16(kB, koff + 64u * c2);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vr[i] = buf_load16(i < 4 ? vA : vB, voff + (uint32_t)(4 * (i & 3)) * (kD * 2));
+    } else {
+      const uint32_t o = (uint32_t)blk * (kD * 2);
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        kr[c2] = buf_load16(rk, o + koff + 64u * c2);
+        kr[4 + c2] = buf_load16(rk, o + 16u * (kD * 2) + koff + 64u * c2);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vr[i] = buf_load16(rv, o + voff + (uint32_t)(4 * i) * (kD * 2));
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vr[i] = buf_load16(rv, o + voff + (uint32_t)(4 * i) * (kD * 2));
   };
 
   issue(0);
@@ -251,7 +292,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, int chunk, hipStream_t stream) {
   const long grid = (long)a.B * a.Hkv * a.splits;
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
+  if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((long)a.B * a.H)), dim3(64 * kCombineWaves), 0, stream,

@@ -57,7 +57,17 @@ struct DecodeArgs {
   int splits;
   float* part_o;    // [B, H, splits, d]
   float* part_lse;  // [B, H, splits]
+  // paged cache (block_table != null): k, v are [num_pages, Hkv, 2^page_shift, d]
+  // and sequence b's logical page p is physical page block_table[b*max_pages + p]
+  const int32_t* block_table;
+  int max_pages;
+  int page_shift;
+  int num_pages;
 };
+
+// Most page-table entries one decode split stages in LDS (a split covers at
+// most this many pages plus one).
+constexpr int kDecodeMaxSplitPages = 2047;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -115,6 +115,37 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* stream);
 
 /*
+ * attn_decode_paged -- attn_decode over a paged KV cache.
+ *
+ * The cache lives in fixed-size pages found through a per-sequence block
+ * table (the PagedAttention scheme that the CANN ops-transformer FlashAttention
+ * page lists under KV-cache management, Kwon et al. 2023 in the FlashAttention
+ * (TH) page's bibliography).  The result is that of attn_decode on the cache
+ * gathered in logical order; the split kernel reads each page in place.
+ *
+ *   k_pages, v_pages  bf16 [num_pages, Hkv, page_size, d]
+ *   block_table       int32 [B, max_pages_per_seq], device memory: logical
+ *                     page p of sequence b (keys p*page_size .. +page_size-1)
+ *                     is physical page block_table[b][p]; entries are clamped
+ *                     to [0, num_pages).
+ *   seqlens_k         int32 [B], device memory, clamped to
+ *                     [0, max_pages_per_seq * page_size]; keys at or beyond
+ *                     it are never read, even inside the last page.
+ *   page_size         a power of two in [16, 1024].
+ *   q, o, lse, H, Hkv, d, scale, num_splits: as attn_decode, with
+ *   Lmax = max_pages_per_seq * page_size.  Workspace: at least
+ *   attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, num_splits) bytes.
+ *   A split may span at most 2047 pages; a call whose splits would span more
+ *   returns FATTN_ERR_UNSUPPORTED (use more splits or larger pages).
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seqlens_k,
+                      void* o, float* lse, int B, int H, int Hkv, int page_size,
+                      int max_pages_per_seq, int num_pages, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * attn_hstu_jagged -- HSTU pointwise attention over packed variable-length
  * sequences (no padding).
  *

@@ -156,6 +156,41 @@ def test_hstu_empty_calls_launch_nothing():
     _hstu(q=0, k=0, v=0, o=0, offsets=0, max_seqlen=0)
 
 
+def _paged(**kw):
+    B, H, Hkv, psz, mp, d = 2, 8, 2, 16, 8, 128
+    ws = fa.attn_decode_workspace_bytes(B, H, Hkv, psz * mp, d, 0)
+    args = dict(q=P, k_pages=P, v_pages=P, block_table=P, seqlens_k=P, o=P, lse=None, B=B, H=H,
+                Hkv=Hkv, page_size=psz, max_pages_per_seq=mp, num_pages=64, d=d, scale=0.1, num_splits=0,
+                workspace=P, workspace_bytes=ws)
+    args.update(kw)
+    fa.attn_decode_paged(stream=S0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_table=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(page_size=8), fa.FATTN_ERR_INVALID_ARG),
+    (dict(page_size=48), fa.FATTN_ERR_INVALID_ARG),
+    (dict(page_size=2048), fa.FATTN_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(num_pages=0), fa.FATTN_ERR_INVALID_ARG),
+    (dict(workspace_bytes=16), fa.FATTN_ERR_INVALID_ARG),
+    (dict(num_splits=65), fa.FATTN_ERR_INVALID_ARG),
+    (dict(d=64), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(H=6, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
+    # one split over 100000 pages of 16 rows: more than a split may stage
+    (dict(max_pages_per_seq=100000, num_splits=1, workspace_bytes=1 << 30), fa.FATTN_ERR_UNSUPPORTED),
+])
+def test_attn_decode_paged_rejects(kw, status):
+    with pytest.raises(fa.FattnError) as e:
+        _paged(**kw)
+    assert e.value.status == status
+    assert fa.fattn_last_error().startswith("attn_decode_paged")
+
+
+def test_paged_empty_batch_launches_nothing():
+    _paged(q=0, k_pages=0, v_pages=0, block_table=0, seqlens_k=0, o=0, workspace=0, B=0)
+
+
 def _bwd(**kw):
     B, H, Hkv, N, d = 2, 4, 2, 100, 128
     ws = fa.attn_bwd_workspace_bytes(B, H, N)

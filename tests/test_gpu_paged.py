@@ -1,0 +1,107 @@
+"""Parity of the paged-cache decode (``attn_decode_paged`` through the C ABI)
+against the fp64 oracle, and against the contiguous decode on the same data.
+
+The pages hold the same cache as the contiguous tests, scattered in a seeded
+random physical order; spare pages and rows past each sequence's length are
+NaN, so any read outside the valid rows would show in the output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import exact_attention_11_amd as fa
+import oracle
+from synthgen import bf16_bits_to_f64
+from synthgen import workloads as W
+
+from _util import assert_bf16, assert_lse, bf16_dev_to_f64, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_paged(px: W.PagedDecodeInputs, splits: int):
+    x = px.base
+    c = x.case
+    mp = px.block_table.shape[1]
+    q, kp, vp = to_dev_bf16(x.q), to_dev_bf16(px.k_pages), to_dev_bf16(px.v_pages)
+    table, sl = to_dev(px.block_table), to_dev(x.seqlens)
+    o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
+    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, mp * px.page_size, c.d, splits)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    fa.attn_decode_paged(q, kp, vp, table, sl, o, lse, c.B, c.H, c.Hkv, px.page_size, mp, px.num_pages, c.d,
+                         c.scale, splits, ws, nbytes)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_contiguous(x: W.DecodeInputs, splits: int, Lmax: int):
+    c = x.case
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
+    o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
+    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, Lmax, c.d, splits)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    fa.attn_decode(q, k, v, to_dev(x.seqlens), o, lse, c.B, c.H, c.Hkv, c.Lmax, c.d, c.scale, splits, ws, nbytes)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def paged_ref(px: W.PagedDecodeInputs):
+    x = px.base
+    f = bf16_bits_to_f64
+    return oracle.decode_paged(f(x.q), f(px.k_pages), f(px.v_pages), px.block_table, x.seqlens, x.case.scale)
+
+
+@pytest.mark.parametrize("P", [16, 32, 64, 256])
+@pytest.mark.parametrize("G", [1, 4, 16])
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+def test_paged_small_every_element(P, G, splits):
+    _need_gpu()
+    Hkv = 2
+    c = W.Decode("paged_small", 5, G * Hkv, Hkv, 700, 128, 1 / math.sqrt(128), 1, 700, 51)
+    x = W.decode_inputs(c, seqlens=[1, 17, 0, 513, 700])
+    px = W.paged_from_decode(x, P, perm_seed=G * 100 + splits)
+    o, lse = run_paged(px, splits)
+    O_ref, L_ref = paged_ref(px)
+    o64, l64 = bf16_dev_to_f64(o), lse.cpu().numpy()
+    tag = f"P={P} G={G} splits={splits}"
+    assert np.all(o64[2] == 0) and np.all(np.isneginf(l64[2])), tag
+    keep = [0, 1, 3, 4]
+    assert_bf16(o64[keep], O_ref[keep], tag)
+    assert_lse(l64[keep], L_ref[keep], tag)
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_paged_matches_contiguous_bitwise(P):
+    # the same rows in the same order: the paged kernel differs only in where
+    # it reads them from
+    _need_gpu()
+    c = W.Decode("paged_vs_contig", 3, 16, 4, 1024, 128, 1 / math.sqrt(128), 1, 1024, 52)
+    x = W.decode_inputs(c, seqlens=[1000, 1024, 33])
+    px = W.paged_from_decode(x, P)
+    o1, l1 = run_paged(px, 8)
+    o2, l2 = run_contiguous(x, 8, c.Lmax)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_full_paged_decode_gqa(P):
+    """The decode workload (B=16, H=32, Hkv=8, L_b in [16384, 32768]) in pages
+    of P rows, every output compared."""
+    _need_gpu()
+    px = W.paged_from_decode(W.decode_inputs(W.DECODE_GQA), P)
+    o, lse = run_paged(px, 0)
+    O_ref, L_ref = paged_ref(px)
+    assert_bf16(bf16_dev_to_f64(o), O_ref, f"paged P={P}")
+    assert_lse(lse.cpu().numpy(), L_ref, f"paged P={P}")
