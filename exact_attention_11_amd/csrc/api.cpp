@@ -156,8 +156,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     return fail(FATTN_ERR_INVALID_ARG, "%s: num_splits must be 0 (auto) or 1..64 (got %d)", fn, num_splits);
   const int G = H / Hkv;
   if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8 or 16)", fn, G);
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16 && G != 32)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8, 16 or 32)", fn, G);
   if (B == 0) return ok();
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || !workspace)
     return fail(FATTN_ERR_INVALID_ARG, "%s: q, caches, seqlens_k, o and workspace must be non-null", fn);
@@ -210,8 +210,8 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     return fail(FATTN_ERR_INVALID_ARG, "%s: num_splits must be 0 (auto) or 1..64 (got %d)", fn, num_splits);
   const int G = H / Hkv;
   if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8 or 16)", fn, G);
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16 && G != 32)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8, 16 or 32)", fn, G);
   if (B == 0) return ok();
   if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !o || !workspace)
     return fail(FATTN_ERR_INVALID_ARG, "%s: q, pages, block_table, seqlens_k, o and workspace must be non-null",

@@ -57,6 +57,7 @@ __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | (((r >> 2)
 //                                      reads, P^T straight from the scores)
 template <int G, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chunk) {
+  constexpr int NT = G > 16 ? G / 16 : 1;  // 16-column tiles of query heads
   __shared__ __attribute__((aligned(16))) unsigned char sv[32 * kD * 2];
   // paged cache: physical page of each logical page this split touches
   __shared__ int pt[PAGED ? kDecodeMaxSplitPages + 2 : 1];
@@ -108,20 +109,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
     }
   }
 
-  // Q^T operand: column n16 = head h0 + n16 (zero for n16 >= G), d = 32c + 8*g4 .. +8
-  bf16x8 qf[4];
+  // Q^T operand of column tile t: column n16 = head h0 + 16t + n16 (zero past
+  // the group), d = 32c + 8*g4 .. +8
+  bf16x8 qf[NT][4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (n16 < G) t = ldg16((const uint16_t*)a.q + ((long)b * a.H + h0 + n16) * kD + 32 * c + 8 * g4);
-    qf[c] = as_bf16x8(t);
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (16 * t + n16 < G) x = ldg16((const uint16_t*)a.q + ((long)b * a.H + h0 + 16 * t + n16) * kD + 32 * c + 8 * g4);
+      qf[t][c] = as_bf16x8(x);
+    }
 
-  f32x4v acc[8];
+  f32x4v acc[NT][8];
+  float m[NT], l[NT];  // running (base-2, scaled) max of column n16 / this lane's share of its sum
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;  // running (base-2, scaled) max of column n16
-  float l = 0.f;      // this lane's share of the running sum
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[t][i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    m[t] = kNegInf;
+    l[t] = 0.f;
+  }
   const float c = a.c;
 
   // per-lane offsets: K operand rows n16 and 16 + n16 of a block, d = 32c + 8*g4;
@@ -169,12 +177,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
 
   issue(0);
   for (int blk = 0; blk < n; blk += 32) {
-    // S^T for keys blk .. blk+15 (sa) and blk+16 .. blk+31 (sb)
-    f32x4v sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    // S^T for keys blk .. blk+15 (sa) and blk+16 .. blk+31 (sb), per column tile
+    f32x4v sa[NT], sb[NT];
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[c2]), qf[c2], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[4 + c2]), qf[c2], sb, 0, 0, 0);
+    for (int t = 0; t < NT; ++t) {
+      sa[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      sb[t] = sa[t];
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[c2]), qf[t][c2], sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[4 + c2]), qf[t][c2], sb[t], 0, 0, 0);
+      }
     }
     // V block -> LDS (natural [key][d] layout, swizzled chunks)
 #pragma unroll
@@ -184,33 +197,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
     }
     if (blk + 32 < n) issue(blk + 32);
 
-    // scores of this lane: keys blk + 4*g4 + r (sa) and blk + 16 + 4*g4 + r (sb)
-    float sc[8];
+    bf16x8 pb[NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = (blk + 4 * g4 + r < n) ? sa[r] * c : kNegInf;
-      sc[4 + r] = (blk + 16 + 4 * g4 + r < n) ? sb[r] * c : kNegInf;
-    }
-    float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = max_xor32(mt);
-    if (wave_any(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m - mn);
-      m = mn;
-      l *= alpha;
+    for (int t = 0; t < NT; ++t) {
+      // scores of this lane: keys blk + 4*g4 + r (sa) and blk + 16 + 4*g4 + r (sb)
+      float sc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-    }
-    float p[8];
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = (blk + 4 * g4 + r < n) ? sa[t][r] * c : kNegInf;
+        sc[4 + r] = (blk + 16 + 4 * g4 + r < n) ? sb[t][r] * c : kNegInf;
+      }
+      float mt =
+          fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = max_xor32(mt);
+      if (wave_any(mt > m[t] + kRescaleSlack)) {
+        const float mn = fmaxf(m[t], mt);
+        const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m[t] - mn);
+        m[t] = mn;
+        l[t] *= alpha;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2_hw(sc[e] - m);  // m is finite: every block has a valid key
-      l += p[e];
+        for (int i = 0; i < 8; ++i) acc[t][i] *= alpha;
+      }
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_hw(sc[e] - m[t]);  // m is finite: every block has a valid key
+        l[t] += p[e];
+      }
+      const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+      pb[t] = as_bf16x8(pw);
     }
-    const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    const bf16x8 pb = as_bf16x8(pw);
 
     // O^T += V^T P^T: slots 0-3 = keys 4*g4 + t, slots 4-7 = keys 16 + 4*g4 + t
 #pragma unroll
@@ -221,21 +239,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
       const u32x2 lo = lds_read_tr16(sv + r0 * (kD * 2) + ((chunk0 ^ v_swz(r0)) << 4) + byte);
       const u32x2 hi = lds_read_tr16(sv + r1 * (kD * 2) + ((chunk0 ^ v_swz(r1)) << 4) + byte);
       const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pb[t], acc[t][db], 0, 0, 0);
     }
   }
 
   // row sum over the four 16-lane groups; normalise and write the partial
-  float lt = l + __shfl_xor(l, 16, 64);
-  lt = sum_xor32(lt);
-  if (n16 < G) {
-    const float inv = 1.f / lt;
-    float* dst = po + (long)n16 * S * kD + 4 * g4;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      stg16(dst + 16 * db, u32x4{__float_as_uint(acc[db][0] * inv), __float_as_uint(acc[db][1] * inv),
-                                 __float_as_uint(acc[db][2] * inv), __float_as_uint(acc[db][3] * inv)});
-    if (g4 == 0) pl[(long)n16 * S] = (m + log2_hw(lt)) * kLn2;
+  for (int t = 0; t < NT; ++t) {
+    float lt = l[t] + __shfl_xor(l[t], 16, 64);
+    lt = sum_xor32(lt);
+    const int hh = 16 * t + n16;  // head within the group
+    if (hh < G) {
+      const float inv = 1.f / lt;
+      float* dst = po + (long)hh * S * kD + 4 * g4;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        stg16(dst + 16 * db, u32x4{__float_as_uint(acc[t][db][0] * inv), __float_as_uint(acc[t][db][1] * inv),
+                                   __float_as_uint(acc[t][db][2] * inv), __float_as_uint(acc[t][db][3] * inv)});
+      if (g4 == 0) pl[(long)hh * S] = (m[t] + log2_hw(lt)) * kLn2;
+    }
   }
 }
 
@@ -331,6 +355,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     case 4: return launch_g<4>(a, chunk, stream);
     case 8: return launch_g<8>(a, chunk, stream);
     case 16: return launch_g<16>(a, chunk, stream);
+    case 32: return launch_g<32>(a, chunk, stream);
     default: return hipErrorInvalidValue;
   }
 }

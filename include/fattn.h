@@ -100,7 +100,8 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  *              O = 0 and LSE = -inf.
  *   o          bf16 [B, H, d]            written
  *   lse        f32  [B, H]               written, or NULL
- *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16}; d == 128; scale finite, >= 0.
+ *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16, 32} (32: multi-query
+ *              attention with 32 heads); d == 128; scale finite, >= 0.
  *   num_splits 0 = automatic (about one work item per resident wave), else 1..64: the
  *              key range [0, Lmax) is cut into num_splits equal chunks
  *              (rounded up to whole 32-key blocks); split s of sequence b

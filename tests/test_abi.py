@@ -109,7 +109,7 @@ def _dec(**kw):
     (dict(scale=-1.0), fa.FATTN_ERR_INVALID_ARG),
     (dict(d=64), fa.FATTN_ERR_UNSUPPORTED),
     (dict(H=6, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
-    (dict(H=64, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(H=128, Hkv=2), fa.FATTN_ERR_UNSUPPORTED),
 ])
 def test_attn_decode_rejects(kw, status):
     with pytest.raises(fa.FattnError) as e:

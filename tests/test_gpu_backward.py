@@ -82,6 +82,20 @@ def test_bwd_gqa_group_of_four_and_wide_scores(causal):
     assert_grad(bf16_dev_to_f64(dv), rv, "dV")
 
 
+def test_bwd_multi_query_one_kv_head():
+    # every query head reads the single kv head: dK and dV sum over all eight
+    _need_gpu()
+    B, H, Hkv, N, d = 1, 8, 1, 130, 64
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = _inputs(79, B, H, Hkv, N, d)
+    dq, dk, dv = run_bwd(q, k, v, do, B, H, Hkv, N, d, scale, 1)
+    rq, rk, rv = oracle.attention_backward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v),
+                                           bf16_bits_to_f64(do), scale, True)
+    assert_grad(bf16_dev_to_f64(dq), rq, "dQ")
+    assert_grad(bf16_dev_to_f64(dk), rk, "dK")
+    assert_grad(bf16_dev_to_f64(dv), rv, "dV")
+
+
 def test_bwd_deterministic():
     _need_gpu()
     B, H, Hkv, N, d = 1, 4, 1, 257, 64

@@ -63,7 +63,7 @@ def paged_ref(px: W.PagedDecodeInputs):
 
 
 @pytest.mark.parametrize("P", [16, 32, 64, 256])
-@pytest.mark.parametrize("G", [1, 4, 16])
+@pytest.mark.parametrize("G", [1, 4, 16, 32])
 @pytest.mark.parametrize("splits", [0, 1, 3, 7])
 def test_paged_small_every_element(P, G, splits):
     _need_gpu()

@@ -95,6 +95,33 @@ def test_bf16_small_every_element(d, N, causal):
     assert_lse(lse.cpu().numpy(), L_ref, f"N={N} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bf16_multi_query_one_kv_head(causal):
+    # multi-query attention: every query head reads the single kv head
+    _need_gpu()
+    B, H, Hkv, N, d = 2, 8, 1, 150, 128
+    scale = 1.0 / math.sqrt(d)
+    q = normal_bf16(61, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(61, TENSOR_K, (B, Hkv, N, d))
+    v = normal_bf16(61, TENSOR_V, (B, Hkv, N, d))
+    o, lse = run_fwd(q, k, v, B, H, Hkv, N, d, scale, causal)
+    O_ref, L_ref = oracle.attention_forward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), scale,
+                                            bool(causal))
+    assert_bf16(bf16_dev_to_f64(o), O_ref, f"MQA causal={causal}")
+    assert_lse(lse.cpu().numpy(), L_ref, f"MQA causal={causal}")
+
+
+def test_decode_multi_query_32_heads():
+    # 32 query heads on one kv head, the longest lengths of the decode workload
+    _need_gpu()
+    c = W.Decode("decode_mqa", 4, 32, 1, 4096, 128, 1 / math.sqrt(128), 1, 4096, 33)
+    x = W.decode_inputs(c, seqlens=[4096, 1, 2500, 3333])
+    o, lse = run_decode(x, 0)
+    O_ref, L_ref = decode_ref(x)
+    assert_bf16(o, O_ref, "MQA decode")
+    assert_lse(lse, L_ref, "MQA decode")
+
+
 def test_bf16_causal_row_zero_is_exactly_v0():
     _need_gpu()
     B, H, N, d = 1, 3, 200, 128
@@ -221,7 +248,7 @@ def decode_ref(x: W.DecodeInputs, batches=None):
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3, 7, 64])
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32])
 def test_decode_small(splits, G):
     _need_gpu()
     Hkv = 2
