@@ -82,7 +82,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              float scale, int causal, void* stream) {
   int st = check_dense("attn_fwd", q, k, v, o, lse, B, H, Hkv, N, scale, causal);
   if (st != FATTN_OK) return st;
-  if (d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "attn_fwd: d=%d not supported (64 or 128)", d);
+  if (d != 64 && d != 128 && d != 256)
+    return fail(FATTN_ERR_UNSUPPORTED, "attn_fwd: d=%d not supported (64, 128 or 256)", d);
   if (B == 0 || N == 0) return ok();
   // K/V rows of one head are addressed with 32-bit byte offsets
   if ((double)N * d * 2 >= 4294967296.0) return fail(FATTN_ERR_INVALID_ARG, "attn_fwd: N*d too large for one head");

@@ -59,6 +59,13 @@ struct Cfg<128> {
   static constexpr int BN = 64;
 };
 template <>
+struct Cfg<256> {
+  // 32-key tiles: the d = 256 output accumulator (128 registers per lane) and
+  // Q fragments (64) leave no room for more; one workgroup per CU, one wave
+  // per SIMD, accumulators in the AGPR half of the register file
+  static constexpr int BN = 32;
+};
+template <>
 struct Cfg<64> {
   static constexpr int BN = 128;
 };
@@ -74,7 +81,7 @@ struct Lds {
   // XOR applied to the 16-byte chunk index of V row r: the 4 consecutive rows a
   // transposing read touches land on disjoint banks (bits >= 2 of the chunk
   // index only, so 32-byte pieces stay contiguous).
-  __device__ static __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
+  __device__ static __forceinline__ int vswz(int r) { return D >= 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
 };
 
 // In-block key order of the first product: swap bits 2 and 3.
@@ -88,7 +95,7 @@ __device__ __forceinline__ int acc_key(int e, int g2) {
 }
 
 template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
-__global__ __launch_bounds__(kThreads, 2) void tile_kernel(TileArgs a, int nq) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void tile_kernel(TileArgs a, int nq) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-row blocks of d
@@ -380,6 +387,7 @@ hipError_t launch_tile_bf16(const TileArgs& a, hipStream_t stream) {
   if (a.epi == Epilogue::Softmax) {
     if (a.d == 128) return launch_causal<128, Epilogue::Softmax, false>(a, stream);
     if (a.d == 64) return launch_causal<64, Epilogue::Softmax, false>(a, stream);
+    if (a.d == 256) return launch_causal<256, Epilogue::Softmax, false>(a, stream);
   } else {
     if (a.d == 128) return launch_causal<128, Epilogue::Silu, true>(a, stream);
     if (a.d == 64) return launch_causal<64, Epilogue::Silu, true>(a, stream);

@@ -53,7 +53,7 @@ extern "C" {
  *   k, v bf16 [B, Hkv, N, d]   query head h reads key/value head h / (H/Hkv)
  *   o    bf16 [B, H,   N, d]   written
  *   lse  f32  [B, H,   N]      written (natural log), or NULL to skip
- *   H % Hkv == 0; d in {64, 128}; scale finite and >= 0;
+ *   H % Hkv == 0; d in {64, 128, 256}; scale finite and >= 0;
  *   causal in {0, 1}: 1 lets row i see keys j <= i.
  *   B == 0 or N == 0 is a valid empty call (nothing launched).
  */

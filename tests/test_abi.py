@@ -66,7 +66,7 @@ def _fwd(fn, **kw):
     (dict(scale=float("inf")), fa.FATTN_ERR_INVALID_ARG),
     (dict(scale=-0.5), fa.FATTN_ERR_INVALID_ARG),
     (dict(d=96), fa.FATTN_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FATTN_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FATTN_ERR_UNSUPPORTED),
 ])
 def test_attn_fwd_rejects(kw, status):
     with pytest.raises(fa.FattnError) as e:

@@ -122,6 +122,29 @@ def test_decode_multi_query_32_heads():
     assert_lse(lse, L_ref, "MQA decode")
 
 
+@pytest.mark.parametrize("N", [1, 7, 33, 129, 300])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_bf16_d256_every_element(N, causal):
+    _need_gpu()
+    B, H, Hkv, d = 2, 4, 2, 256
+    scale = 1.0 / math.sqrt(d)
+    q = normal_bf16(400 + N, TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(400 + N, TENSOR_K, (B, Hkv, N, d))
+    v = normal_bf16(400 + N, TENSOR_V, (B, Hkv, N, d))
+    o, lse = run_fwd(q, k, v, B, H, Hkv, N, d, scale, causal)
+    O_ref, L_ref = oracle.attention_forward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), scale,
+                                            bool(causal))
+    assert_bf16(bf16_dev_to_f64(o), O_ref, f"d=256 N={N} causal={causal}")
+    assert_lse(lse.cpu().numpy(), L_ref, f"d=256 N={N} causal={causal}")
+
+
+def test_bf16_d256_long_sampled_rows():
+    # B=2, H=16, N=4096, d=256 causal: sampled rows of three heads
+    _need_gpu()
+    c = W.Dense("prefill_d256", 2, 16, 16, 4096, 256, 1.0 / 16.0, True, "bf16", 1005)
+    _full_size_check(c, [(0, 0), (1, 9), (1, 15)])
+
+
 def test_bf16_causal_row_zero_is_exactly_v0():
     _need_gpu()
     B, H, N, d = 1, 3, 200, 128
