@@ -9,6 +9,8 @@ is already resident in HBM:
   3. attn_hstu_jagged  16 jagged sequences, L_b in [512, 4096], H=4, d=64
   4. attn_bwd     backward of step 1 (dQ, dK, dV for a synthetic dO)
   5. attn_decode_paged  step 2's cache in pages of 16 rows, shuffled
+  6. attn_hstu_jagged on step 3's sequences zero-padded to 4096 rows (the dense-padded
+     baseline the HSTU page compares jagged tensors against; ``hstu_padded``)
 
 ``value`` is the prefill throughput in TFLOP/s with the FLOP convention of the
 ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
@@ -17,7 +19,7 @@ backward TFLOP/s (five products, 5 n^2 d per (b, h) causal) are reported
 beside it.  Prints ONE JSON line.
 
 Other modes (used for profiling, see profiles/):
-  --only prefill|decode|hstu|backward|decode_paged   run just that part of the step
+  --only prefill|decode|hstu|backward|decode_paged|hstu_padded   run just that part of the step
   --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
   --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
   --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
@@ -63,7 +65,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded"],
+                    default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -246,7 +249,7 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
         return 0
 
-    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward", "decode_paged"]
+    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded"]
     print(f"bench: preparing inputs for {parts}", file=sys.stderr, flush=True)
 
     pc = W.PREFILL_D128_CAUSAL
@@ -299,8 +302,26 @@ def main(argv=None) -> int:
                                                  dc.scale, args.splits, ws, wsb)
     jc = W.HSTU_JAGGED
     jx = None
-    if "hstu" in parts:
+    if "hstu" in parts or "hstu_padded" in parts:
         jx = W.jagged_inputs(jc)
+    if "hstu_padded" in parts:
+        # every sequence zero-padded to len_hi rows: silu(alpha q.0) = 0, so the
+        # padding adds nothing to the valid rows but is computed like them
+        Np = jc.len_hi
+        nseq_p = len(jx.lengths)
+        padded = {}
+        for name in ("q", "k", "v"):
+            src = getattr(jx, name)
+            dst = np.zeros((nseq_p * Np, jc.H, jc.d), dtype=np.uint16)
+            for b in range(nseq_p):
+                s0, s1 = int(jx.offsets[b]), int(jx.offsets[b + 1])
+                dst[b * Np:b * Np + (s1 - s0)] = src[s0:s1]
+            padded[name] = bf16(dst)
+        poff = torch.arange(0, (nseq_p + 1) * Np, Np, dtype=torch.int32, device=dev)
+        po_h = torch.empty((nseq_p * Np, jc.H, jc.d), dtype=torch.bfloat16, device=dev)
+        calls["hstu_padded"] = lambda: fa.attn_hstu_jagged(padded["q"], padded["k"], padded["v"], po_h, poff, nseq_p,
+                                                           jc.H, jc.d, Np, jc.alpha, jc.inv_n, 1)
+    if "hstu" in parts:
         T = int(jx.offsets[-1])
         jq, jk, jv = bf16(jx.q), bf16(jx.k), bf16(jx.v)
         joff = torch.from_numpy(jx.offsets).to(dev)
@@ -396,6 +417,13 @@ def main(argv=None) -> int:
                            "ms_per_call": round(ms["backward"], 4), "flops": bf}
         if out["value"] is None:
             out.update({"value": round(bt, 2), "unit": "TFLOP/s"})
+    if "hstu_padded" in parts:
+        out["hstu_padded"] = {"ms_per_call": round(ms["hstu_padded"], 4), "padded_to": jc.len_hi,
+                              "sequences": len(jx.lengths)}
+        if "hstu" in parts:
+            out["hstu_padded"]["jagged_speedup"] = round(ms["hstu_padded"] / ms["hstu"], 3)
+        if out["value"] is None:
+            out.update({"value": round(ms["hstu_padded"], 4), "unit": "ms", "higher_is_better": False})
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(px, pc, args.cpu_seconds)

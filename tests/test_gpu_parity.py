@@ -342,6 +342,35 @@ def test_hstu_small_every_element(d, causal):
         assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
 
 
+@pytest.mark.parametrize("causal", [0, 1])
+def test_hstu_dense_padded_equals_jagged(causal):
+    """Sequences zero-padded to a common length and run as equal-length
+    sequences give the jagged result on every valid row (silu(0) = 0, so the
+    zero keys and values contribute nothing), bitwise."""
+    _need_gpu()
+    c = W.Jagged("hstu_pad", 4, 2, 64, 1, 300, 0.3, 1.0 / 64, bool(causal), 42, 1.0)
+    x = W.jagged_inputs(c, lengths=[300, 7, 0, 129])
+    o = run_hstu(x, causal)
+    Np = 300
+    pad = {}
+    for name in ("q", "k", "v"):
+        src = getattr(x, name)
+        dst = np.zeros((4 * Np, c.H, c.d), dtype=np.uint16)
+        for b in range(4):
+            s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
+            dst[b * Np:b * Np + (s1 - s0)] = src[s0:s1]
+        pad[name] = to_dev_bf16(dst)
+    po = torch.empty((4 * Np, c.H, c.d), dtype=torch.bfloat16, device="cuda")
+    off = torch.arange(0, 5 * Np, Np, dtype=torch.int32, device="cuda")
+    fa.attn_hstu_jagged(pad["q"], pad["k"], pad["v"], po, off, 4, c.H, c.d, Np, c.alpha, c.inv_n, causal)
+    torch.cuda.synchronize()
+    got = po.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = o  # jagged result, f64 view of bf16
+    for b in range(4):
+        s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert np.array_equal(bf16_bits_to_f64(got[b * Np:b * Np + (s1 - s0)]), ref[s0:s1]), f"seq {b}"
+
+
 def test_full_hstu_jagged():
     _need_gpu()
     c = W.HSTU_JAGGED
