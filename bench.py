@@ -11,6 +11,7 @@ is already resident in HBM:
   5. attn_decode_paged  step 2's cache in pages of 16 rows, shuffled
   6. attn_hstu_jagged on step 3's sequences zero-padded to 4096 rows (the dense-padded
      baseline the HSTU page compares jagged tensors against; ``hstu_padded``)
+  7. attn_fwd_fp8  step 1's shape with E4M3 Q, K, V and per-head descales
 
 ``value`` is the prefill throughput in TFLOP/s with the FLOP convention of the
 ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
@@ -19,7 +20,7 @@ backward TFLOP/s (five products, 5 n^2 d per (b, h) causal) are reported
 beside it.  Prints ONE JSON line.
 
 Other modes (used for profiling, see profiles/):
-  --only prefill|decode|hstu|backward|decode_paged|hstu_padded   run just that part of the step
+  --only prefill|decode|hstu|backward|decode_paged|hstu_padded|prefill_fp8   run just that part of the step
   --copy-calib                 run a plain 1 GiB device copy (HBM counter calibration)
   --summarize-trace DIR        summarise a rocprofv3 --kernel-trace --stats run
   --summarize-pmc DIR          summarise a rocprofv3 --pmc run (per-kernel bytes)
@@ -45,6 +46,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
 TILE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/tile_bf16.hip", "exact_attention_11_amd/csrc/common.hpp",
                        "exact_attention_11_amd/csrc/launch.hpp"]
 DECODE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/decode.hip", "exact_attention_11_amd/csrc/common.hpp",
@@ -65,8 +67,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded"],
-                    default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded",
+                                       "prefill_fp8"], default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -249,7 +251,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
         return 0
 
-    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded"]
+    parts = [args.only] if args.only else ["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded",
+                                           "prefill_fp8"]
     print(f"bench: preparing inputs for {parts}", file=sys.stderr, flush=True)
 
     pc = W.PREFILL_D128_CAUSAL
@@ -271,6 +274,17 @@ def main(argv=None) -> int:
         calls["prefill"]()  # the backward reads the forward's O and LSE
         calls["backward"] = lambda: fa.attn_bwd(q, k, v, o, lse, gout, gq, gk, gv, pc.B, pc.H, pc.Hkv, pc.N, pc.d,
                                                 pc.scale, 1, bws, bwsb)
+    if "prefill_fp8" in parts:
+        fc = W.PREFILL_FP8
+        fx = W.fp8_dense_inputs(fc)
+        dev_arr = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        fq, fk, fv = dev_arr(fx.q), dev_arr(fx.k), dev_arr(fx.v)
+        fdq, fdk, fdv = dev_arr(fx.descale_q), dev_arr(fx.descale_k), dev_arr(fx.descale_v)
+        fo = torch.empty((fc.B, fc.H, fc.N, fc.d), dtype=torch.bfloat16, device=dev)
+        flse = torch.empty((fc.B, fc.H, fc.N), dtype=torch.float32, device=dev)
+        calls["prefill_fp8"] = lambda: fa.attn_fwd_fp8(fq, fk, fv, fo, flse, fdq, fdk, fdv, fc.B, fc.H, fc.Hkv, fc.N,
+                                                       fc.d, fc.scale, 1)
+        del fx
     dc = W.DECODE_GQA
     dx = None
     if "decode" in parts or "decode_paged" in parts:
@@ -417,6 +431,13 @@ def main(argv=None) -> int:
                            "ms_per_call": round(ms["backward"], 4), "flops": bf}
         if out["value"] is None:
             out.update({"value": round(bt, 2), "unit": "TFLOP/s"})
+    if "prefill_fp8" in parts:
+        ff = 2 * fc.N * fc.N * fc.d * fc.B * fc.H
+        ft = ff / (ms["prefill_fp8"] * 1e-3) / 1e12
+        out["prefill_fp8"] = {"TFLOP/s": round(ft, 2), "frac_fp8_peak": round(ft / PEAK_FP8_TFLOPS, 4),
+                              "ms_per_call": round(ms["prefill_fp8"], 4), "flops": ff}
+        if out["value"] is None:
+            out.update({"value": round(ft, 2), "unit": "TFLOP/s"})
     if "hstu_padded" in parts:
         out["hstu_padded"] = {"ms_per_call": round(ms["hstu_padded"], 4), "padded_to": jc.len_hi,
                               "sequences": len(jx.lengths)}

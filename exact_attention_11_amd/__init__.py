@@ -20,6 +20,7 @@ __all__ = [
     "FattnLibraryError",
     "attn_fwd",
     "attn_fwd_f32",
+    "attn_fwd_fp8",
     "attn_decode",
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
@@ -39,6 +40,7 @@ _LIB_PATH = os.path.join(_PKG, "libfattn.so")
 EXPORTED_SYMBOLS = (
     "attn_fwd",
     "attn_fwd_f32",
+    "attn_fwd_fp8",
     "attn_decode_workspace_bytes",
     "attn_decode",
     "attn_decode_paged",
@@ -79,6 +81,7 @@ _sz = ctypes.c_size_t
 _SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
@@ -164,6 +167,14 @@ def attn_fwd_f32(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, stream=None):
     st = library().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Hkv), int(N),
                                 int(d), float(scale), int(causal), _stream(stream))
     _check("attn_fwd_f32", st)
+
+
+def attn_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, Hkv, N, d, scale, causal, stream=None):
+    """FP8 (E4M3) fused attention; see ``attn_fwd_fp8`` in include/fattn.h."""
+    st = library().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(descale_q), _ptr(descale_k),
+                                _ptr(descale_v), int(B), int(H), int(Hkv), int(N), int(d), float(scale), int(causal),
+                                _stream(stream))
+    _check("attn_fwd_fp8", st)
 
 
 def attn_decode_workspace_bytes(B, H, Hkv, lmax_hint, d, num_splits) -> int:

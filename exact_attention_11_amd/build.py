@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "tile_bf16.hip", "prefill_f32.hip", "decode.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "tile_bf16.hip", "prefill_f32.hip", "decode.hip", "bwd_bf16.hip", "tile_fp8.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed f32 VALU ops.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

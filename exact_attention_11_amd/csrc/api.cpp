@@ -132,6 +132,36 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(fattn::launch_prefill_f32(a, static_cast<hipStream_t>(stream)), "attn_fwd_f32 launch");
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* descale_q,
+                 const float* descale_k, const float* descale_v, int B, int H, int Hkv, int N, int d, float scale,
+                 int causal, void* stream) {
+  const char* fn = "attn_fwd_fp8";
+  int st = check_dense(fn, q, k, v, o, lse, B, H, Hkv, N, scale, causal);
+  if (st != FATTN_OK) return st;
+  if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
+  if (B == 0 || N == 0) return ok();
+  if (!descale_q || !descale_k || !descale_v)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: descale_q, descale_k and descale_v must be non-null", fn);
+  if ((double)N * d >= 4294967296.0) return fail(FATTN_ERR_INVALID_ARG, "%s: N*d too large for one head", fn);
+  fattn::Fp8Args a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.descale_q = descale_q;
+  a.descale_k = descale_k;
+  a.descale_v = descale_v;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.c = scale * kLog2e;
+  a.causal = causal;
+  return hip_status(fattn::launch_tile_fp8(a, static_cast<hipStream_t>(stream)), "attn_fwd_fp8 launch");
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits) {
   if (B < 0 || H < 1 || Hkv < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;
   int s = num_splits;

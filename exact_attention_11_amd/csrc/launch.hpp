@@ -74,6 +74,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Automatic split count for a decode shape.
 int decode_auto_splits(int B, int Hkv, int Lmax);
 
+struct Fp8Args {
+  const void* q;            // [B, H, N, d] E4M3
+  const void* k;            // [B, Hkv, N, d] E4M3
+  const void* v;
+  void* o;                  // [B, H, N, d] bf16
+  float* lse;               // [B, H, N] or null
+  const float* descale_q;   // [B, H]: real value = fp8 * descale
+  const float* descale_k;   // [B, Hkv]
+  const float* descale_v;   // [B, Hkv]
+  int B, H, Hkv, N, d;
+  float c;                  // scale * log2(e)
+  int causal;
+};
+
+// FP8 (E4M3) prefill tile kernel.
+hipError_t launch_tile_fp8(const Fp8Args& a, hipStream_t stream);
+
 struct BwdArgs {
   const void* q;      // [B, H, N, d] bf16
   const void* k;      // [B, Hkv, N, d] bf16

@@ -70,6 +70,26 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* ls
                  void* stream);
 
 /*
+ * attn_fwd_fp8 -- attn_fwd with FP8 inputs: q, k, v in OCP FP8 E4M3 (one
+ * byte each), one f32 descale per (batch, head) slice of each (the real value
+ * is fp8 * descale), both products on the FP8 matrix cores with f32
+ * accumulation, o in bf16.  The FlashAttention (TH) page's FlashAttention-3
+ * section names FP8 as a lever but gives no scaling convention; this is the
+ * per-head one.  The probabilities are rounded to E4M3 before the P V
+ * product, which bounds the accuracy (about 2^-4 relative per weight).
+ *
+ *   q          E4M3 [B, H, N, d];  descale_q f32 [B, H]   (device memory)
+ *   k, v       E4M3 [B, Hkv, N, d]; descale_k, descale_v f32 [B, Hkv]
+ *   o          bf16 [B, H, N, d] written;  lse f32 [B, H, N] written, or NULL
+ *   d == 128; the other arguments as attn_fwd.  Descales are read on the
+ *   device; they must be finite and > 0.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const float* descale_q, const float* descale_k, const float* descale_v,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 void* stream);
+
+/*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for this
  * shape: room for one partial output row (f32, d values) and one partial
  * log-sum-exp (f32) per (b, h, split), rounded up to 256 bytes.

@@ -63,6 +63,62 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 value
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP FP8 E4M3 (1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits, no infinities; nearest, ties to even); return uint8 bits.
+
+    Magnitudes beyond 448 saturate to +-448; NaN maps to 0x7F.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
+    a = np.minimum(np.abs(np.nan_to_num(x, nan=0.0)), E4M3_MAX)
+    # exponent of the binade (normal numbers from 2^-6); subnormals share 2^-6's spacing 2^-9
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)                  # spacing of representable values in the binade
+    q = np.rint(a / step) * step           # round half to even on the exact quotient
+    # rounding up may reach the next binade: recompute its fields from q
+    with np.errstate(divide="ignore"):
+        e2 = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    normal = q >= 2.0 ** -6
+    e2 = np.where(normal, np.clip(e2, -6, 8), -6)
+    mant = np.where(normal, q / np.exp2(e2) - 1.0, q / 2.0 ** -6) * 8.0
+    exp_field = np.where(normal, e2 + 7, 0)
+    bits = (exp_field.astype(np.uint8) << np.uint8(3)) | np.rint(mant).astype(np.uint8)
+    bits = bits | sign
+    bits[np.isnan(np.asarray(x))] = np.uint8(0x7F)
+    return bits
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 bit patterns as float64 (0x7F / 0xFF are NaN)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = s * v
+    return np.where((b & 0x7F) == 0x7F, np.nan, v)
+
+
+def normal_e4m3(seed: int, tensor_id: int, shape, scale_axes: int = 2, sigma: float = 1.0):
+    """i.i.d. N(0, sigma^2) values (as drawn by normal_f32) quantised to E4M3
+    with one float32 descale per leading ``scale_axes``-index (e.g. per
+    (batch, head)): descale = amax / 448, bits = round(x / descale).  The
+    tensor's value is bits * descale.  Returns (uint8 bits, float32 descale)."""
+    x = normal_f32(seed, tensor_id, shape, sigma)
+    lead = shape[:scale_axes]
+    flat = x.reshape(int(np.prod(lead)), -1)
+    amax = np.abs(flat).max(axis=1)
+    descale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    bits = f32_to_e4m3_bits((flat / descale[:, None]).astype(np.float32))
+    return bits.reshape(shape), descale.reshape(lead)
+
+
 _CHUNK = 1 << 22
 
 

@@ -38,7 +38,9 @@ from . import (
     TENSOR_Q,
     TENSOR_V,
     bf16_bits_to_f64,
+    e4m3_bits_to_f64,
     normal_bf16,
+    normal_e4m3,
     normal_f32,
     offsets_from_lengths,
     uniform_lengths,
@@ -95,6 +97,7 @@ PREFILL_D64 = Dense("prefill_d64", 1, 32, 32, 4096, 64, 1.0 / 8.0, True, "bf16",
 PREFILL_D128_CAUSAL = Dense("prefill_d128_causal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), True, "bf16", 1002)
 PREFILL_D128_FULL = Dense("prefill_d128_noncausal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), False, "bf16", 1002)
 PREFILL_LONG = Dense("prefill_long", 1, 32, 32, 32768, 128, 1.0 / math.sqrt(128.0), True, "bf16", 1002)
+PREFILL_FP8 = Dense("prefill_fp8_d128_causal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), True, "fp8", 1006)
 DECODE_GQA = Decode("decode_gqa", 16, 32, 8, 32768, 128, 1.0 / math.sqrt(128.0), 16384, 32768, 1003)
 HSTU_JAGGED = Jagged("hstu_jagged", 16, 4, 64, 512, 4096, 1.0 / 8.0, 1.0 / 4096.0, True, 1004)
 
@@ -143,6 +146,31 @@ def decode_inputs(c: Decode, seqlens=None) -> DecodeInputs:
         k[b, :, seqlens[b]:, :] = BF16_QNAN
         v[b, :, seqlens[b]:, :] = BF16_QNAN
     return DecodeInputs(c, q, k, v, seqlens)
+
+
+@dataclass
+class Fp8DenseInputs:
+    case: Dense
+    q: np.ndarray         # E4M3 bits (uint8) [B, H, N, d]
+    k: np.ndarray         # [B, Hkv, N, d]
+    v: np.ndarray
+    descale_q: np.ndarray  # float32 [B, H]: value = bits * descale
+    descale_k: np.ndarray  # float32 [B, Hkv]
+    descale_v: np.ndarray
+
+    def f64(self, name: str, index=()) -> np.ndarray:
+        bits = getattr(self, name)[index]
+        ds = getattr(self, "descale_" + name)[index[:2] if isinstance(index, tuple) else index]
+        return e4m3_bits_to_f64(bits) * ds.astype(np.float64)[..., None, None]
+
+
+def fp8_dense_inputs(c: Dense) -> Fp8DenseInputs:
+    """Q, K, V drawn as normal_f32 (sigma) and quantised to E4M3 with one
+    descale per (batch, head)."""
+    q, dq = normal_e4m3(c.seed, TENSOR_Q, (c.B, c.H, c.N, c.d), 2, c.sigma)
+    k, dk = normal_e4m3(c.seed, TENSOR_K, (c.B, c.Hkv, c.N, c.d), 2, c.sigma)
+    v, dv = normal_e4m3(c.seed, TENSOR_V, (c.B, c.Hkv, c.N, c.d), 2, c.sigma)
+    return Fp8DenseInputs(c, q, k, v, dq, dk, dv)
 
 
 @dataclass
