@@ -16,14 +16,21 @@
 //    dQ^T += K^T dS^T with K^T gathered by transposing LDS reads.  It also
 //    computes delta for its rows (from dO and O, already in registers for the
 //    fragment loads) and stores it for the second kernel.
-//  * bwd_dkdv_kernel, one workgroup per 64 keys of a (batch, kv-head), 16 keys
-//    per wave as the columns of 16x16x32 products: per step of 64 query rows
-//    (of every query head of the group) S = Q K^T and dP = dO V^T, then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T gathered by
-//    transposing reads.  The group's query heads accumulate in registers.
-// Q/dO (second kernel) and K/V (first kernel) tiles stream into LDS with
-// direct HBM->LDS loads, double buffered, one barrier per tile.  Causal tiles
-// wholly above the diagonal are skipped, straddling tiles masked per element.
+//  * bwd_dkdv_kernel, one workgroup of 8 waves per 128 keys of a (batch,
+//    kv-head): four wave pairs of 32 keys each, the keys being the columns of
+//    32x32x16 products.  Per tile of 64 query rows (of every query head of
+//    the group) the first wave of a pair computes S = Q K^T, P, and
+//    dV^T += dO^T P; the second, one tile behind, dP = dO V^T, dS with the P
+//    its partner left in LDS, and dK^T += Q^T dS; dO^T and Q^T come from
+//    transposing reads.  Splitting the products over the pair keeps each
+//    wave's registers (one K or V operand, one accumulator) within the half of
+//    the register file that two waves per SIMD allow, while 32 keys per wave
+//    halve the LDS bytes per product against 16.  The group's query heads
+//    accumulate in registers.
+// K/V tiles (first kernel) stream into LDS double buffered, Q/dO tiles
+// (second kernel) into a ring of three, with direct HBM->LDS loads and one
+// barrier per tile.  Causal tiles wholly above the diagonal are skipped,
+// straddling tiles masked per element.
 #include <cfloat>
 
 #include "common.hpp"
@@ -34,25 +41,21 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBM = 128;  // query rows per dQ workgroup (32 per wave)
-constexpr int kBN = 64;   // keys per dQ tile and per dK/dV workgroup (16 per wave)
+constexpr int kBN = 64;   // keys per dQ tile
 constexpr int kBQ = 64;   // query rows per step of the dK/dV loop
+constexpr int kKB = 128;  // keys per dK/dV workgroup (32 per wave pair)
+constexpr int kPairThreads = 512;
 
-// XOR on the 16-byte chunk index of row r of a K or V tile (dQ kernel).  The
-// plain operand reads (16 lanes, 16 consecutive rows, one logical chunk) and
-// the transposing reads (4 consecutive rows, 32 bytes each) both fall on
-// distinct banks.
+// XOR on the 16-byte chunk index of row r of a K or V tile (dQ kernel) or a Q
+// or dO tile (dK/dV kernel).  The plain operand reads (16 lanes, 16
+// consecutive rows, one logical chunk) and the transposing reads (4
+// consecutive rows, 32 bytes each) both fall on distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_kv(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
-// Same for the Q and dO tiles of the dK/dV kernel, whose plain reads touch
-// rows 8a + 4e + b (a, b = 0..3, e fixed) of a 32-row group.
-template <int D>
-__device__ __forceinline__ int swz_q(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 3) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 3) & 3));
-}
-
-// In-block key order of the first products of the dQ kernel: swap bits 2, 3.
+// In-block row order of the first products (keys in the dQ kernel, queries in
+// the dK/dV kernel): swap bits 2, 3.
 __device__ __forceinline__ int key_perm(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // Key (relative to the 32-key block) held by accumulator element e = 4j + r of
@@ -252,21 +255,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+__global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
   constexpr int ROW = D * 2;
-  constexpr int QT = kBQ * ROW;         // bytes of a Q or dO tile
-  constexpr int SLOT = 2 * QT + 2048;   // Q, dO, LSE (1 KB), delta (1 KB)
-  constexpr int NLD = QT / 1024 / 4;    // 1 KB direct loads per wave per tile
-  constexpr int NDS = D / 32;           // k-steps over d of the 16x16x32 products
-  constexpr int NDB = D / 16;           // 16-row blocks of d in the accumulators
-  static_assert(QT % 4096 == 0, "tile split over four waves");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SLOT];
+  constexpr int QT = kBQ * ROW;        // bytes of a Q or dO tile
+  constexpr int SLOT = 2 * QT + 2048;  // Q, dO, LSE (1 KB), delta (1 KB)
+  constexpr int NSLOT = 3;             // tiles u-1 (second waves), u (first waves), u+1 (loading)
+  constexpr int PBUF = kBQ * 32 * 2;   // P of one pair and tile, bf16
+  constexpr int NLD = QT / 1024 / 8;   // 1 KB direct loads per wave, tensor and tile
+  constexpr int NDC = D / 16;          // k-steps over d of the first products
+  constexpr int NDB = D / 32;          // 32-row blocks of d in the accumulators
+  static_assert(QT % 8192 == 0, "tile split over eight waves");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NSLOT * SLOT + 2 * 4 * PBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int pair = wv & 3;
+  const bool first = wv < 4;  // S, P, dV; the other wave of the pair does dP, dS, dK
+  const int n32 = lane & 31;
+  const int g2 = lane >> 5;
 
   // (batch, kv-head, key block); the first key blocks carry the most causal
   // work and go first; all blocks of a kv-head on one XCD
@@ -279,194 +286,202 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int nk
   const int b = bg / a.Hkv;
   const int N = a.N;
   const int grp = a.H / a.Hkv;
-  const int k0 = kblk * kBN;
-  const int kw0 = k0 + 16 * wv;  // this wave's first key
-  const int key = kw0 + l16;     // this lane's key (column of the products)
+  const int k0 = kblk * kKB;
+  const int kp0 = k0 + 32 * pair;  // the pair's first key
+  const int key = kp0 + n32;       // this lane's key: column of every product
   const bool key_ok = key < N;
   const long kbase = ((long)b * a.Hkv + g) * N * D;
 
-  // K^T and V^T fragments (B operands): column = key, k = d 32s + 8g4 .. +8
-  bf16x8 kf[NDS], vf[NDS];
+  // B operand of the first product, kept in registers: K^T (first wave) or
+  // V^T (second wave); column n32 = key, d = 16c + 8g2 .. +8
+  bf16x8 bop[NDC];
+  {
+    const uint16_t* src = (const uint16_t*)(first ? a.k : a.v) + kbase + (long)key * D + 8 * g2;
 #pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    u32x4 tk = {0u, 0u, 0u, 0u}, tv = tk;
-    if (key_ok) {
-      const long off = kbase + (long)key * D + 32 * s + 8 * g4;
-      tk = ldg16((const uint16_t*)a.k + off);
-      tv = ldg16((const uint16_t*)a.v + off);
+    for (int c = 0; c < NDC; ++c) {
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (key_ok) t = ldg16(src + 16 * c);
+      bop[c] = as_bf16x8(t);
     }
-    kf[s] = as_bf16x8(tk);
-    vf[s] = as_bf16x8(tv);
   }
-
-  f32x4 dk[NDB], dv[NDB];
+  // dV^T (first wave) or dK^T / scale (second wave): row d, column key
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
   const int nqb = (N + kBQ - 1) / kBQ;
-  const int i0 = CAUSAL ? kblk : 0;  // kBQ == kBN: query block kblk holds the diagonal
+  const int i0 = CAUSAL ? k0 / kBQ : 0;  // first query tile reaching the block's keys
   const int per_head = nqb - i0;
-  const int steps = grp * per_head;
+  const int steps = grp * per_head;      // (query head of the group, query tile)
 
-  // Q/dO tile loads: wave instruction i fills LDS bytes (wv + 4i) KB .. +1 KB
+  // Q/dO tile loads: wave instruction i fills LDS bytes (wv + 8i) KB .. +1 KB;
+  // the swizzle is applied through the source address
   uint32_t toff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int byte = (wv + 4 * i) * 1024 + 16 * lane;
+    const int byte = (wv + 8 * i) * 1024 + 16 * lane;
     const int r = byte / ROW;
     const int pc = (byte % ROW) / 16;
-    toff[i] = (uint32_t)r * ROW + (uint32_t)(pc ^ swz_q<D>(r)) * 16u;
+    toff[i] = (uint32_t)r * ROW + (uint32_t)(pc ^ swz_kv<D>(r)) * 16u;
   }
   const uint32_t lds0 = lds_addr_of(smem);
-  auto load_step = [&](int t) {
-    const int hh = t / per_head;
-    const int r0 = (i0 + t % per_head) * kBQ;
+  auto load_tile = [&](int u) {
+    const int hh = u / per_head;
+    const int r0 = (i0 + u % per_head) * kBQ;
     const long rowbase = ((long)b * a.H + g * grp + hh) * N + r0;
     const uint32_t bytes = (uint32_t)(N - r0) * ROW;  // rows r0 .. N-1
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + rowbase * D, bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const uint16_t*)a.dout + rowbase * D, bytes);
-    const uint32_t st = lds0 + (uint32_t)(t & 1) * SLOT;
+    const uint32_t st = lds0 + (uint32_t)(u % NSLOT) * SLOT;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_dma16(rq, st + (wv + 4 * i) * 1024, toff[i]);
+    for (int i = 0; i < NLD; ++i) lds_dma16(rq, st + (wv + 8 * i) * 1024, toff[i]);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) lds_dma16(rd, st + QT + (wv + 4 * i) * 1024, toff[i]);
+    for (int i = 0; i < NLD; ++i) lds_dma16(rd, st + QT + (wv + 8 * i) * 1024, toff[i]);
     // LSE and delta of rows r0 .. r0+63 (1 KB of LDS each; lanes past the 64
     // values land in the unused rest of the region)
     if (wv == 0) lds_dma16(make_rsrc(a.lse + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT, 16u * lane);
     if (wv == 1) lds_dma16(make_rsrc(a.delta + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT + 1024, 16u * lane);
   };
 
+  // transposing reads of dO^T / Q^T: row offset within the 8-query group and
+  // (chunk, byte) of the 4 d values this lane addresses
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
   const float c2 = a.c;
-  load_step(0);
-  for (int t = 0; t < steps; ++t) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < steps) load_step(t + 1);
-    const int r0 = (i0 + t % per_head) * kBQ;
-    const unsigned char* sq = smem + (t & 1) * SLOT;
+
+  // Step t: the first wave of each pair works on tile t and leaves P in LDS;
+  // the second works on tile t-1 with the P its partner left there one step
+  // earlier.  One barrier per step orders the DMA of tile t+1 (into the slot
+  // tile t-2 used), the P hand-over and the reuse of the two P buffers.
+  load_tile(0);
+  for (int t = 0; t <= steps; ++t) {
+    wait_vmem();      // this wave's pieces of tile t have landed
+    __syncthreads();  // everyone's have; tile t-2's slot and P buffer are free
+    if (t + 1 < steps) load_tile(t + 1);
+    const int u = first ? t : t - 1;
+    if (u < 0 || u >= steps) continue;
+    const int r0 = (i0 + u % per_head) * kBQ;
+    if (CAUSAL && r0 + kBQ - 1 < kp0) continue;  // every query precedes every key of the pair
+    const unsigned char* sq = smem + (u % NSLOT) * SLOT;
     const unsigned char* sdo = sq + QT;
     const float* sl = reinterpret_cast<const float*>(sq + 2 * QT);
     const float* sd = sl + 256;
+    unsigned char* pbuf = smem + NSLOT * SLOT + ((u & 1) * 4 + pair) * PBUF;
 
-    // row values of this lane: rows r0 + 32 t2 + 8 g4 + 4e + r
-    float nl[2][8], dl[2][8];
+    // S = Q K^T (first wave) or dP = dO V^T (second wave), queries on the M
+    // side in key_perm order: accumulator element e of block mb is query
+    // r0 + 32 mb + acc_key(e, g2), so each lane's 8 values of a 16-query step
+    // are 8 consecutive queries (the B operand of the second product)
+    const unsigned char* sa = first ? sq : sdo;
+    f32x16 s[2];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl + 32 * t2 + 8 * g4);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(sl + 32 * t2 + 8 * g4 + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(sd + 32 * t2 + 8 * g4);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(sd + 32 * t2 + 8 * g4 + 4);
+    for (int c = 0; c < NDC; ++c) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        nl[t2][r] = -l0[r] * kLog2e;
-        nl[t2][4 + r] = -l1[r] * kLog2e;
-        dl[t2][r] = d0[r];
-        dl[t2][4 + r] = d1[r];
+      for (int mb = 0; mb < 2; ++mb) {
+        const int qr = 32 * mb + key_perm(n32);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sa + qr * ROW + (((2 * c + g2) ^ swz_kv<D>(qr)) << 4));
+        const f32x16 zero = {};
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), bop[c], c == 0 ? zero : s[mb], 0, 0, 0);
       }
     }
 
-    // S = Q K^T and dP = dO V^T: row block rb = 2 t2 + e holds, in accumulator
-    // row 4 g + r, query 32 t2 + 8 g + 4e + r, so each lane's 8 values of a
-    // 32-query step are 8 consecutive queries (the B operand of the next
-    // products); the A operand rows are read in that permuted order
-    f32x4 s[4], dp[4];
+    // B operand of the second product as bf16 pairs: P (first wave) or
+    // dS = P (dP - delta) (second wave); P goes through LDS lane for lane
+    uint32_t w[2][8];
+    if (first) {
+      const bool masked = (CAUSAL && r0 < kp0 + 31) || (r0 + kBQ > N);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int qr = 32 * (rb >> 1) + 8 * (l16 >> 2) + 4 * (rb & 1) + (l16 & 3);
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 lv[4];
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const int off = qr * ROW + (((4 * ds + g4) ^ swz_q<D>(qr)) << 4);
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(sq + off);
-        const u32x4 ad = *reinterpret_cast<const u32x4*>(sdo + off);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aq), kf[ds], ds == 0 ? zero : s[rb], 0, 0, 0);
-        dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ad), vf[ds], ds == 0 ? zero : dp[rb], 0, 0, 0);
-      }
-    }
-    if ((CAUSAL && r0 < kw0 + 15) || (r0 + kBQ > N) || (kw0 + 16 > N)) {
+        for (int j = 0; j < 4; ++j)
+          lv[j] = *reinterpret_cast<const f32x4*>(sl + 32 * mb + 16 * (j >> 1) + 8 * g2 + 4 * (j & 1));
+        float p[16];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = r0 + 32 * (rb >> 1) + 8 * g4 + 4 * (rb & 1) + r;
-          if (!(key_ok && row < N && (!CAUSAL || key <= row))) s[rb][r] = kNegInf;
+        for (int e = 0; e < 16; ++e) {
+          float x = s[mb][e];
+          if (masked) {
+            const int row = r0 + 32 * mb + acc_key(e, g2);
+            if (!(row < N && (!CAUSAL || key <= row))) x = kNegInf;
+          }
+          p[e] = exp2_hw(__builtin_fmaf(x, c2, -lv[e >> 2][e & 3] * kLog2e));
         }
-    }
-    // P and dS as bf16 pairs: step t2, dwords 2e and 2e+1 = queries 8g4 + 4e + 0..3
-    uint32_t pw[2][4], sw[2][4];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float p[4], x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = exp2_hw(__builtin_fmaf(s[2 * t2 + e][r], c2, nl[t2][4 * e + r]));
-          x[r] = p[r] * (dp[2 * t2 + e][r] - dl[t2][4 * e + r]);
-        }
-        pw[t2][2 * e] = pack_bf16x2(p[0], p[1]);
-        pw[t2][2 * e + 1] = pack_bf16x2(p[2], p[3]);
-        sw[t2][2 * e] = pack_bf16x2(x[0], x[1]);
-        sw[t2][2 * e + 1] = pack_bf16x2(x[2], x[3]);
+        for (int i = 0; i < 8; ++i) w[mb][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(pbuf + mb * 2048 + 16 * lane) = u32x4{w[mb][0], w[mb][1], w[mb][2], w[mb][3]};
+        *reinterpret_cast<u32x4*>(pbuf + mb * 2048 + 1024 + 16 * lane) = u32x4{w[mb][4], w[mb][5], w[mb][6], w[mb][7]};
       }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 dv4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          dv4[j] = *reinterpret_cast<const f32x4*>(sd + 32 * mb + 16 * (j >> 1) + 8 * g2 + 4 * (j & 1));
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(pbuf + mb * 2048 + 16 * lane);
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(pbuf + mb * 2048 + 1024 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t pw = i < 4 ? p0[i] : p1[i - 4];
+          const int e0 = 2 * i, e1 = 2 * i + 1;
+          const float x0 = bf16_lo(pw) * (s[mb][e0] - dv4[e0 >> 2][e0 & 3]);
+          const float x1 = bf16_hi(pw) * (s[mb][e1] - dv4[e1 >> 2][e1 & 3]);
+          w[mb][i] = pack_bf16x2(x0, x1);
+        }
+      }
+    }
 
-    // dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T by transposing reads:
-    // lane l16 of group g4 gets d = 16 db + l16 for queries 32 t2 + 8 g4 + 0..7
+    // dV^T += dO^T P (first wave) or dK^T += Q^T dS (second wave); dO^T and
+    // Q^T gathered by transposing reads
+    const unsigned char* sb = first ? sdo : sq;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const u32x4 pv = {pw[t2][0], pw[t2][1], pw[t2][2], pw[t2][3]};
-      const u32x4 sv = {sw[t2][0], sw[t2][1], sw[t2][2], sw[t2][3]};
-      const int ra = 32 * t2 + 8 * g4 + (l16 >> 2);
-      const int rc = ra + 4;
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int ch = 2 * db + ((l16 & 3) >> 1);
-        const int oa = ra * ROW + ((ch ^ swz_q<D>(ra)) << 4) + 8 * (l16 & 1);
-        const int oc = rc * ROW + ((ch ^ swz_q<D>(rc)) << 4) + 8 * (l16 & 1);
-        const u32x2 dlo = lds_read_tr16(sdo + oa);
-        const u32x2 dhi = lds_read_tr16(sdo + oc);
-        const u32x2 qlo = lds_read_tr16(sq + oa);
-        const u32x2 qhi = lds_read_tr16(sq + oc);
-        const u32x4 dt = {dlo[0], dlo[1], dhi[0], dhi[1]};
-        const u32x4 qt = {qlo[0], qlo[1], qhi[0], qhi[1]};
-        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(dt), as_bf16x8(pv), dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qt), as_bf16x8(sv), dk[db], 0, 0, 0);
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 pw = {w[mb][4 * jj], w[mb][4 * jj + 1], w[mb][4 * jj + 2], w[mb][4 * jj + 3]};
+        const int qrow = 32 * mb + 16 * jj + 8 * g2 + tr_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int ch = 4 * db + tr_chunk;
+          const u32x2 lo = lds_read_tr16(sb + qrow * ROW + ((ch ^ swz_kv<D>(qrow)) << 4) + tr_byte);
+          const u32x2 hi = lds_read_tr16(sb + (qrow + 4) * ROW + ((ch ^ swz_kv<D>(qrow + 4)) << 4) + tr_byte);
+          const u32x4 at = {lo[0], lo[1], hi[0], hi[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at), as_bf16x8(pw), acc[db], 0, 0, 0);
+        }
       }
     }
   }
 
   if (!key_ok) return;
-  // accumulator row 4 g4 + r of block db is d = 16 db + 4 g4 + r of this key
-  const float sc = a.scale;
-  uint16_t* dkrow = (uint16_t*)a.dk + kbase + (long)key * D;
-  uint16_t* dvrow = (uint16_t*)a.dv + kbase + (long)key * D;
+  // accumulator row 8 jq + 4 g2 + r of block db is d = 32 db + 8 jq + 4 g2 + r of this key
+  const float f = first ? 1.f : a.scale;
+  uint16_t* dst = (uint16_t*)(first ? a.dv : a.dk) + kbase + (long)key * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    u32x2 tk, tv;
-    tk[0] = pack_bf16x2(dk[db][0] * sc, dk[db][1] * sc);
-    tk[1] = pack_bf16x2(dk[db][2] * sc, dk[db][3] * sc);
-    tv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
-    tv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
-    stg8(dkrow + 16 * db + 4 * g4, tk);
-    stg8(dvrow + 16 * db + 4 * g4, tv);
-  }
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      u32x2 t;
+      t[0] = pack_bf16x2(acc[db][4 * jq] * f, acc[db][4 * jq + 1] * f);
+      t[1] = pack_bf16x2(acc[db][4 * jq + 2] * f, acc[db][4 * jq + 3] * f);
+      stg8(dst + 32 * db + 8 * jq + 4 * g2, t);
+    }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t stream) {
   const int nq = (a.N + kBM - 1) / kBM;
   const long g1 = (long)nq * a.H * a.B;
-  const int nkb = (a.N + kBN - 1) / kBN;
+  const int nkb = (a.N + kKB - 1) / kKB;
   const long g2 = (long)nkb * a.Hkv * a.B;
   if (g1 <= 0) return hipSuccess;
   if (g1 > 0x7fffffffL || g2 > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(kThreads), 0, stream, a, nq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(kThreads), 0, stream, a, nkb);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(kPairThreads), 0, stream, a, nkb);
   return hipGetLastError();
 }
 
