@@ -52,22 +52,31 @@ constexpr int kThreads = 256;
 constexpr int kBM = 128;              // query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
+// Keys per K/V tile.  Smaller tiles leave room for more waves per SIMD: with
+// 32-key tiles the d = 128 kernel needs at most 168 registers and 33 KB of LDS,
+// so three workgroups (12 waves) share a CU; the d = 64 kernel fits four
+// (at most 128 registers, 34 KB).  Every wave's step is a serial chain
+// (products, softmax, products); more waves per SIMD keep the matrix cores fed
+// while some of them are in the softmax.
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<128> {
-  static constexpr int BN = 64;
+  static constexpr int BN = 32;
+  static constexpr int kWavesPerSimd = 3;
 };
 template <>
 struct Cfg<256> {
-  // 32-key tiles: the d = 256 output accumulator (128 registers per lane) and
-  // Q fragments (64) leave no room for more; one workgroup per CU, one wave
-  // per SIMD, accumulators in the AGPR half of the register file
+  // the d = 256 output accumulator (128 registers per lane) and Q fragments
+  // (64) leave no room for more; one workgroup per CU, one wave per SIMD,
+  // accumulators in the AGPR half of the register file
   static constexpr int BN = 32;
+  static constexpr int kWavesPerSimd = 1;
 };
 template <>
 struct Cfg<64> {
-  static constexpr int BN = 128;
+  static constexpr int BN = 64;
+  static constexpr int kWavesPerSimd = 4;
 };
 
 template <int D, int BN>
@@ -95,7 +104,7 @@ __device__ __forceinline__ int acc_key(int e, int g2) {
 }
 
 template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void tile_kernel(TileArgs a, int nq) {
+__global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(TileArgs a, int nq) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-row blocks of d

@@ -17,7 +17,8 @@
 // FMA and descale_v into the final 1/l.  One workgroup of four waves owns 128
 // query rows of one (batch, head), 32 per wave; K and V tiles of 64 keys are
 // staged through double-buffered LDS (register-staged buffer loads, rows past
-// the sequence end read as zero).
+// the sequence end read as zero).  At most 168 registers per lane, so three
+// workgroups (12 waves) share a CU.
 //
 // Lane layouts of the 32x32x64 FP8 product (A, B: lane l holds row / column
 // l % 32 and k = 32 (l / 32) .. +32, one byte each; C as the 32x32 bf16
@@ -60,7 +61,7 @@ __device__ __forceinline__ i32x8 cat(u32x4 lo, u32x4 hi) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void tile_fp8_kernel(Fp8Args a, int nq) {
+__global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq) {
   static_assert(D == 128, "d = 128");
   constexpr int ROW = D;                    // bytes per row
   constexpr int NKC = D / 64;               // 64-wide k-steps over d
