@@ -71,6 +71,9 @@ def parse_args(argv=None):
                                        "prefill_fp8"], default=None)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements after the timed step (other prefill shapes, decode "
+                         "split sweep, GPU clock and power)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -207,6 +210,112 @@ def cpu_baseline(x, case, seconds: float):
         "sample": f"{done} of {len(heads)} (b,h) heads of the B={case.B} H={case.H} N={case.N} d={case.d} "
                   f"{'causal' if case.causal else 'non-causal'} prefill, all rows, fp64 numpy, {el:.1f} s",
     }
+
+
+def _time_calls(fn, stream, warmup: int = 3, reps: int = 10) -> float:
+    """Mean milliseconds per call of fn from HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _sample_clock_and_power(keep_busy, seconds: float = 4.0):
+    """GPU clock (MHz, mean over the XCDs) and socket power (W) read by amd-smi
+    while a second thread keeps launching keep_busy(); None if amd-smi is
+    missing or its output cannot be read."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    stop = threading.Event()
+
+    def launcher():
+        t_end = time.perf_counter() + seconds
+        while not stop.is_set() and time.perf_counter() < t_end:
+            keep_busy()
+
+    th = threading.Thread(target=launcher)
+    th.start()
+    try:
+        time.sleep(0.5)  # let the queue fill and the clock settle
+        r = subprocess.run([exe, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=30)
+    finally:
+        stop.set()
+        th.join()
+        torch.cuda.synchronize()
+    try:
+        data = json.loads(r.stdout)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = [c["clk"]["value"] for name, c in gpu["clock"].items()
+                  if name.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
+                  and isinstance(c["clk"].get("value"), (int, float))]
+        power = gpu["power"]["socket_power"]["value"]
+        return {"gfx_mhz": round(sum(clocks) / len(clocks), 1) if clocks else None,
+                "socket_power_w": power if isinstance(power, (int, float)) else None,
+                "source": "amd-smi metric -c -p, sampled while the headline prefill runs"}
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
+def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl, do, dlse,
+                         headline_tflops):
+    """Other prefill shapes, a decode split sweep and the GPU clock under the
+    headline prefill, each timed with HIP events after the timed step."""
+    import torch
+
+    ctx = {}
+    # the headline shape without the causal mask: 4 n^2 d per (b, h)
+    f = 4 * pc.N * pc.N * pc.d * pc.B * pc.H
+    ms_nc = _time_calls(lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 0), stream)
+    ctx["prefill_noncausal"] = {"workload": "B=8 H=32 N=4096 d=128 bf16 non-causal", "ms_per_call": round(ms_nc, 4),
+                                "TFLOP/s": round(f / (ms_nc * 1e-3) / 1e12, 2),
+                                "frac_bf16_peak": round(f / (ms_nc * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    for key, c, label in (("prefill_long", W.PREFILL_LONG, "B=1 H=32 N=32768 d=128 bf16 causal"),
+                          ("prefill_d64", W.PREFILL_D64, "B=1 H=32 N=4096 d=64 bf16 causal")):
+        x = W.dense_inputs(c)
+        cq, ck, cv = bf16(x.q), bf16(x.k), bf16(x.v)
+        del x
+        co = torch.empty_like(cq)
+        cl = torch.empty((c.B, c.H, c.N), dtype=torch.float32, device=dev)
+        ms_c = _time_calls(lambda: fa.attn_fwd(cq, ck, cv, co, cl, c.B, c.H, c.Hkv, c.N, c.d, c.scale, 1), stream)
+        fc = 2 * c.N * c.N * c.d * c.B * c.H
+        ctx[key] = {"workload": label, "ms_per_call": round(ms_c, 4), "TFLOP/s": round(fc / (ms_c * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(fc / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del cq, ck, cv, co, cl
+    # decode at fixed split counts (the timed step uses the automatic count)
+    ssum = int(dx.seqlens.sum())
+    nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
+    wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, 64)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    sweep = {}
+    for sp in (16, 32, 64):
+        ms_d = _time_calls(lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
+                                                  dc.scale, sp, ws, wsb), stream, reps=20)
+        sweep[str(sp)] = {"GB/s": round(nbytes / (ms_d * 1e-3) / 1e9, 1), "ms_per_call": round(ms_d, 4)}
+    ctx["decode_splits"] = sweep
+    # GPU clock and power under the headline prefill
+    cp = _sample_clock_and_power(lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 1))
+    if cp is not None and cp.get("gfx_mhz"):
+        peak_at_clk = PEAK_BF16_TFLOPS * cp["gfx_mhz"] / 2400.0
+        cp["prefill_peak_at_gfx_clock"] = round(peak_at_clk, 1)
+        cp["prefill_frac_at_gfx_clock"] = round(headline_tflops / peak_at_clk, 4)
+    ctx["clock_under_prefill"] = cp
+    return ctx
 
 
 def main(argv=None) -> int:
@@ -445,6 +554,10 @@ def main(argv=None) -> int:
             out["hstu_padded"]["jagged_speedup"] = round(ms["hstu_padded"] / ms["hstu"], 3)
         if out["value"] is None:
             out.update({"value": round(ms["hstu_padded"], 4), "unit": "ms", "higher_is_better": False})
+    if not args.only and not args.no_context:
+        print("bench: context measurements", file=sys.stderr, flush=True)
+        out["context"] = context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl,
+                                              do, dlse, out["roofline"]["achieved"])
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(px, pc, args.cpu_seconds)
