@@ -184,6 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
     const unsigned char* sk = smem + (j & 1) * 2 * TILE;
     const unsigned char* sv = sk + TILE;
 
+    __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with elementwise work
     // S^T = K Q^T and dP^T = V dO^T (keys on the M side, in key_perm order)
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), df[c], c == 0 ? zero : dp[kb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if ((CAUSAL && k0 + kBN - 1 > q0w) || (k0 + kBN > N)) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -221,6 +223,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
     }
+    __builtin_amdgcn_s_setprio(1);
     // dQ^T += K^T dS^T; K^T fragments gathered by transposing reads
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   if (!row_ok) return;
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
     const float* sd = sl + 256;
     unsigned char* pbuf = smem + NSLOT * SLOT + ((u & 1) * 4 + pair) * PBUF;
 
+    __builtin_amdgcn_s_setprio(1);  // products first: the partner fills the gaps with elementwise work
     // S = Q K^T (first wave) or dP = dO V^T (second wave), queries on the M
     // side in key_perm order: accumulator element e of block mb is query
     // r0 + 32 mb + acc_key(e, g2), so each lane's 8 values of a 16-query step
@@ -388,6 +393,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // B operand of the second product as bf16 pairs: P (first wave) or
     // dS = P (dP - delta) (second wave); P goes through LDS lane for lane
     uint32_t w[2][8];
@@ -434,6 +440,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
       }
     }
 
+    __builtin_amdgcn_s_setprio(1);
     // dV^T += dO^T P (first wave) or dK^T += Q^T dS (second wave); dO^T and
     // Q^T gathered by transposing reads
     const unsigned char* sb = first ? sdo : sq;
@@ -453,6 +460,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   if (!key_ok) return;

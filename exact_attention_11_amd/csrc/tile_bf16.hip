@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
     if (active) {
       const unsigned char* sk = smem + buf * L::stage;
       const unsigned char* sv = sk + L::kBytes;
+      __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
       // S^T = K Q^T
       f32x16 s[NKB];
 #pragma unroll
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
         }
       }
 
+      __builtin_amdgcn_s_setprio(0);
       const bool masked = (CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len);
       // visibility of accumulator element e of 32-key block kb
       auto visible = [&](int kb, int e) {
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
           for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[kb][2 * e], y[kb][2 * e + 1]);
       }
 
+      __builtin_amdgcn_s_setprio(1);
       // O^T += V^T P^T; V^T fragments gathered by transposing reads
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -347,6 +350,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   }

@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
     if (active) {
       const unsigned char* sk = smem + buf * STAGE;
       const unsigned char* sv = sk + TILE;
+      __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
       // S^T = K Q^T: 32-key block kb = LDS rows 32 kb .. +32
       f32x16 s[2];
 #pragma unroll
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
         s[kb] = t;
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // element e of block kb of this lane is key k0 + 32 g2 + 16 kb + e
       if ((CAUSAL && k0 + kBN - 1 > q0w) || (k0 + kBN > N)) {
 #pragma unroll
@@ -240,6 +242,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
           d = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], d, true);
           pb[4 * kb + w] = d;
         }
+      __builtin_amdgcn_s_setprio(1);
       // O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -258,6 +261,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
   }
