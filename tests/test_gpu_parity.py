@@ -294,6 +294,35 @@ def test_decode_zero_length_sequence():
     assert_lse(lse[1:], L_ref)
 
 
+def test_decode_reused_workspace_with_random_contents():
+    """The workspace needs no clearing: random bytes on entry, then calls with
+    other split counts on the same buffer, each checked against the oracle;
+    two calls with equal arguments agree bitwise."""
+    _need_gpu()
+    c = W.Decode("decode_reuse", 3, 16, 4, 900, 128, 1 / math.sqrt(128), 1, 900, 33)
+    x = W.decode_inputs(c, seqlens=[5, 333, 900])
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
+    sl = to_dev(x.seqlens)
+    nbytes = max(fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, c.Lmax, c.d, s) for s in (1, 5, 13, 64))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    O_ref, L_ref = decode_ref(x)
+    prev = None
+    for splits in (13, 13, 5, 64, 1, 13):
+        o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
+        fa.attn_decode(q, k, v, sl, o, lse, c.B, c.H, c.Hkv, c.Lmax, c.d, c.scale, splits, ws, nbytes)
+        torch.cuda.synchronize()
+        got = bf16_dev_to_f64(o)
+        assert_bf16(got, O_ref, f"splits={splits}")
+        assert_lse(lse.cpu().numpy(), L_ref, f"splits={splits}")
+        if splits == 13 and prev is not None:
+            assert np.array_equal(got, prev), "equal calls differ"
+        if splits == 13:
+            prev = got
+
+
 @pytest.mark.parametrize("splits", [0, 16, 64])
 def test_full_decode_gqa(splits):
     _need_gpu()
