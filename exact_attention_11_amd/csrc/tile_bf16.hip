@@ -173,6 +173,13 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   for (int c = 0; c < NDC; ++c) {
     u32x4 t = {0u, 0u, 0u, 0u};
     if (qrow < len) t = ldg16(qp + (long)qrow * row_stride + 16 * c + 8 * g2);
+    if constexpr (EPI == Epilogue::Silu) {
+      // HSTU: Q scaled by log2(e) alpha (rounded to bf16), so the product is
+      // the exponent t of the SiLU weight directly
+      const float beta = a.c * kLog2e;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
+    }
     qf[c] = as_bf16x8(t);
   }
 
@@ -305,14 +312,16 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
           for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
         }
       } else {
-        const float alpha = cexp;
+        // the product is t = log2(e) alpha s (Q carries the factor):
+        // t / (1 + 2^-t) = log2(e) silu(alpha s); the factor log2(e) comes off
+        // in the epilogue's scale
         float y[NKB][16];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float x = s[kb][e] * alpha;
-            y[kb][e] = x * rcp_hw(1.f + exp2_hw(-x * kLog2e));
+            const float t = s[kb][e];
+            y[kb][e] = t * rcp_hw(1.f + exp2_hw(-t));
           }
         if (masked) {
 #pragma unroll
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
       a.lse[lse_base + qrow] = lt > 0.f ? (m_ref + log2_hw(lt)) * kLn2 : kNegInf;
     }
   } else {
-    scale_out = a.inv_n;
+    scale_out = a.inv_n * kLn2;  // the weights carry a factor log2(e)
   }
   uint16_t* orow = op + (long)qrow * row_stride;
 #pragma unroll
