@@ -35,7 +35,10 @@
 //    true running max, so weights stay <= 256 and the final O/l and LSE are
 //    the same quantities.
 //  * Silu: HSTU pointwise attention, silu(alpha s) with no normalisation
-//    (HSTU page, the listing and optimisation one).
+//    (HSTU page, the listing and optimisation one).  Q is multiplied by
+//    alpha*log2(e) as it is loaded, so the product is t = log2(e) alpha s and
+//    a weight is t / (1 + 2^-t) = log2(e) silu(alpha s); the epilogue's 1/n
+//    takes the factor ln 2.
 //
 // Causal masking is generated in the kernel from tile positions: tiles wholly
 // below the diagonal run unmasked, tiles straddling it are masked per element,
