@@ -27,6 +27,7 @@ Other modes (used for profiling, see profiles/):
   --traffic FETCH WRITE CFETCH CWRITE
                                HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE
                                runs, calibrated by the same counters on a 1 GiB copy
+  --traffic-kernel NAME        with --traffic: those bytes for the named kernel(s) instead
 """
 
 from __future__ import annotations
@@ -79,6 +80,9 @@ def parse_args(argv=None):
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
+    ap.add_argument("--traffic-kernel", action="append", default=None, metavar="NAME",
+                    help="with --traffic: report this kernel (substring of its name) instead of the prefill; "
+                         "repeatable")
     return ap.parse_args(argv)
 
 
@@ -103,6 +107,23 @@ def summarize_trace(d: str) -> None:
             name = r.get("Name", r.get("KernelName", "?"))
             print(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                   f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {name[:110]}")
+    # per-dispatch durations: median and the 10th / 90th percentiles
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        per = {}
+        for r in _read_csv(path):
+            name = r.get("Kernel_Name", r.get("Name", "?"))
+            try:
+                per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            except (KeyError, ValueError):
+                continue
+        if not per:
+            continue
+        print(f"# {os.path.relpath(path, d)}: per-dispatch duration percentiles")
+        print(f"{'calls':>6} {'p10_us':>10} {'median_us':>10} {'p90_us':>10}  kernel")
+        for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            ds.sort()
+            pick = lambda f: ds[min(len(ds) - 1, int(round(f * (len(ds) - 1))))]  # noqa: E731
+            print(f"{len(ds):6d} {pick(0.1):10.2f} {pick(0.5):10.2f} {pick(0.9):10.2f}  {name[:110]}")
 
 
 def summarize_pmc(d: str) -> None:
@@ -138,22 +159,35 @@ def _pmc_mean_kib(d: str, kernel_substr: str, counter: str) -> float:
     return sum(vals.values()) / len(vals)
 
 
-def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir) -> None:
-    """Print the traffic summary for the causal d=128 prefill kernel: counter KiB
-    per dispatch scaled so that a 1 GiB device copy reads and writes 1 GiB."""
-    kern = "tile_kernel<128, true, (fattn::Epilogue)0, false>"
+PREFILL_KERNEL = "tile_kernel<128, true, (fattn::Epilogue)0, false>"
+
+
+def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, kernels=None) -> None:
+    """Print HBM bytes per dispatch: counter KiB scaled so that a 1 GiB device
+    copy reads and writes 1 GiB.  Default: the causal d=128 prefill kernel (the
+    summary bench.py reads back); with `kernels`, one block per kernel."""
     copy = "copyBuffer"
     gib = float(1 << 30)
     f_cal = gib / (_pmc_mean_kib(cfetch_dir, copy, "FETCH_SIZE") * 1024.0)
     w_cal = gib / (_pmc_mean_kib(cwrite_dir, copy, "WRITE_SIZE") * 1024.0)
-    fetch = _pmc_mean_kib(fetch_dir, kern, "FETCH_SIZE") * 1024.0 * f_cal
-    write = _pmc_mean_kib(write_dir, kern, "WRITE_SIZE") * 1024.0 * w_cal
     print(f"fetch_calibration: {f_cal:.4f}")
     print(f"write_calibration: {w_cal:.4f}")
-    print(f"hbm_fetch_bytes_per_launch: {fetch:.0f}")
-    print(f"hbm_write_bytes_per_launch: {write:.0f}")
-    print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
-    print(f"kernel_sources_sha: {sources_sha(TILE_KERNEL_SOURCES)}")
+    if not kernels:
+        fetch = _pmc_mean_kib(fetch_dir, PREFILL_KERNEL, "FETCH_SIZE") * 1024.0 * f_cal
+        write = _pmc_mean_kib(write_dir, PREFILL_KERNEL, "WRITE_SIZE") * 1024.0 * w_cal
+        print(f"hbm_fetch_bytes_per_launch: {fetch:.0f}")
+        print(f"hbm_write_bytes_per_launch: {write:.0f}")
+        print(f"hbm_bytes_per_launch: {fetch + write:.0f}")
+        print(f"kernel_sources_sha: {sources_sha(TILE_KERNEL_SOURCES)}")
+        return
+    total = 0.0
+    for kern in kernels:
+        fetch = _pmc_mean_kib(fetch_dir, kern, "FETCH_SIZE") * 1024.0 * f_cal
+        write = _pmc_mean_kib(write_dir, kern, "WRITE_SIZE") * 1024.0 * w_cal
+        total += fetch + write
+        print(f"[{kern}] hbm_fetch_bytes_per_launch: {fetch:.0f}")
+        print(f"[{kern}] hbm_write_bytes_per_launch: {write:.0f}")
+    print(f"hbm_bytes_all_listed_kernels: {total:.0f}")
 
 
 # ----------------------------------------------------------------------------- the benchmark
@@ -327,7 +361,7 @@ def main(argv=None) -> int:
         summarize_pmc(args.summarize_pmc)
         return 0
     if args.traffic:
-        traffic_summary(*args.traffic)
+        traffic_summary(*args.traffic, kernels=args.traffic_kernel)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is described "
