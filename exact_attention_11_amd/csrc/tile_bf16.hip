@@ -107,7 +107,7 @@ __device__ __forceinline__ int acc_key(int e, int g2) {
 }
 
 template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
-__global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(TileArgs a, int nq) {
+__global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(TileArgs a, int nq, int pair) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-row blocks of d
@@ -121,13 +121,17 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
-  // ---- work item: (batch, head, query block), heaviest blocks first, all
-  // blocks of a head on one XCD (dispatch is round-robin over 8 XCDs).
+  // ---- work item: (batch, head, slot), all slots of a head on one XCD
+  // (dispatch is round-robin over 8 XCDs).  Unpaired: slot = one query block,
+  // heaviest first.  Paired (causal grids that fit on the chip at once): slot
+  // i runs query blocks nqb-1-i and i, so every workgroup does the same work
+  // and no CU is left with the heaviest blocks.
   const int G = gridDim.x;
   int wid = blockIdx.x;
   if ((G & 7) == 0) wid = (wid & 7) * (G >> 3) + (wid >> 3);
-  const int qb = nq - 1 - (wid % nq);
-  const int bh = wid / nq;
+  const int nslot = pair ? (nq + 1) / 2 : nq;
+  const int slot = wid % nslot;
+  const int bh = wid / nslot;
   const int h = bh % a.H;
   const int b = bh / a.H;
 
@@ -160,244 +164,261 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
     vp = (const uint16_t*)a.v + kbase;
     lse_base = ((long)b * a.H + h) * a.N;
   }
-  const int q0 = qb * kBM;
-  if (len <= 0 || q0 >= len) return;  // uniform over the workgroup
+  auto run_block = [&](const int qb) {
+    const int q0 = qb * kBM;
+    if (len <= 0 || q0 >= len) return;  // uniform over the workgroup
 
-  const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+    const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
+    const int n_tiles = (kv_end + BN - 1) / BN;
 
-  const int q0w = q0 + 32 * wv;
-  const bool wave_live = q0w < len;
-  const int qrow = q0w + n32;
+    const int q0w = q0 + 32 * wv;
+    const bool wave_live = q0w < len;
+    const int qrow = q0w + n32;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.
-  bf16x8 qf[NDC];
+    // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.
+    bf16x8 qf[NDC];
 #pragma unroll
-  for (int c = 0; c < NDC; ++c) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < len) t = ldg16(qp + (long)qrow * row_stride + 16 * c + 8 * g2);
-    if constexpr (EPI == Epilogue::Silu) {
-      // HSTU: Q scaled by log2(e) alpha (rounded to bf16), so the product is
-      // the exponent t of the SiLU weight directly
-      const float beta = a.c * kLog2e;
+    for (int c = 0; c < NDC; ++c) {
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (qrow < len) t = ldg16(qp + (long)qrow * row_stride + 16 * c + 8 * g2);
+      if constexpr (EPI == Epilogue::Silu) {
+        // HSTU: Q scaled by log2(e) alpha (rounded to bf16), so the product is
+        // the exponent t of the SiLU weight directly
+        const float beta = a.c * kLog2e;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
+        for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
+      }
+      qf[c] = as_bf16x8(t);
     }
-    qf[c] = as_bf16x8(t);
-  }
 
-  // ---- global -> register staging of one K/V tile (buffer loads; rows past
-  // the sequence end read as zero)
-  constexpr int KCH = D / 8;                   // 16-byte chunks per row
-  constexpr int NLD = BN * KCH / kThreads;     // 16-byte loads per thread per tensor
-  const uint32_t row_bytes = (uint32_t)row_stride * 2;
-  uint32_t goff[NLD];  // byte offset of this thread's chunks within a tile
-  int lds_row[NLD], lds_chunk[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int ci = tid + kThreads * i;
-    lds_row[i] = ci / KCH;
-    lds_chunk[i] = ci % KCH;
-    goff[i] = (uint32_t)lds_row[i] * row_bytes + (uint32_t)lds_chunk[i] * 16u;
-  }
-  u32x4 kr[NLD], vr[NLD];
-
-  auto load_tile = [&](int k0) {
-    // valid bytes from row k0: rows k0 .. len-1 of this head
-    const uint32_t bytes = (uint32_t)(len - k0 - 1) * row_bytes + D * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * row_stride, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * row_stride, bytes);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = buf_load16(rk, goff[i]);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = buf_load16(rv, goff[i]);
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* sk = smem + buf * L::stage;
-    unsigned char* sv = sk + L::kBytes;
+    // ---- global -> register staging of one K/V tile (buffer loads; rows past
+    // the sequence end read as zero)
+    constexpr int KCH = D / 8;                   // 16-byte chunks per row
+    constexpr int NLD = BN * KCH / kThreads;     // 16-byte loads per thread per tensor
+    const uint32_t row_bytes = (uint32_t)row_stride * 2;
+    uint32_t goff[NLD];  // byte offset of this thread's chunks within a tile
+    int lds_row[NLD], lds_chunk[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      *reinterpret_cast<u32x4*>(sk + lds_row[i] * L::kRow + lds_chunk[i] * 16) = kr[i];
-      *reinterpret_cast<u32x4*>(sv + lds_row[i] * L::vRow + ((lds_chunk[i] ^ L::vswz(lds_row[i])) << 4)) = vr[i];
+      const int ci = tid + kThreads * i;
+      lds_row[i] = ci / KCH;
+      lds_chunk[i] = ci % KCH;
+      goff[i] = (uint32_t)lds_row[i] * row_bytes + (uint32_t)lds_chunk[i] * 16u;
     }
-  };
+    u32x4 kr[NLD], vr[NLD];
 
-  // per-lane part of the transposing V^T reads: row offset within the 8-key
-  // group and (chunk, byte) of the 4 d values this lane addresses
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_byte = 8 * (lane & 1);
-
-  // ---- accumulators and running statistics
-  f32x16 acc[NDB];
+    auto load_tile = [&](int k0) {
+      // valid bytes from row k0: rows k0 .. len-1 of this head
+      const uint32_t bytes = (uint32_t)(len - k0 - 1) * row_bytes + D * 2;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * row_stride, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * row_stride, bytes);
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
+      for (int i = 0; i < NLD; ++i) kr[i] = buf_load16(rk, goff[i]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-  float m_ref = kNegInf;  // base-2 reference max (scaled)
-  float l_part = 0.f;     // this lane's share of the row sum
-  const float cexp = a.c;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const int k0 = j * BN;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(k0 + BN);
-
-    const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
-    if (active) {
-      const unsigned char* sk = smem + buf * L::stage;
-      const unsigned char* sv = sk + L::kBytes;
-      __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
-      // S^T = K Q^T
-      f32x16 s[NKB];
+      for (int i = 0; i < NLD; ++i) vr[i] = buf_load16(rv, goff[i]);
+    };
+    auto store_tile = [&](int buf) {
+      unsigned char* sk = smem + buf * L::stage;
+      unsigned char* sv = sk + L::kBytes;
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) {
+      for (int i = 0; i < NLD; ++i) {
+        *reinterpret_cast<u32x4*>(sk + lds_row[i] * L::kRow + lds_chunk[i] * 16) = kr[i];
+        *reinterpret_cast<u32x4*>(sv + lds_row[i] * L::vRow + ((lds_chunk[i] ^ L::vswz(lds_row[i])) << 4)) = vr[i];
+      }
+    };
+
+    // per-lane part of the transposing V^T reads: row offset within the 8-key
+    // group and (chunk, byte) of the 4 d values this lane addresses
+    const int tr_row = (lane & 15) >> 2;
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_byte = 8 * (lane & 1);
+
+    // ---- accumulators and running statistics
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    float m_ref = kNegInf;  // base-2 reference max (scaled)
+    float l_part = 0.f;     // this lane's share of the row sum
+    const float cexp = a.c;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+      const int buf = j & 1;
+      const int k0 = j * BN;
+      const bool has_next = j + 1 < n_tiles;
+      if (has_next) load_tile(k0 + BN);
+
+      const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
+      if (active) {
+        const unsigned char* sk = smem + buf * L::stage;
+        const unsigned char* sv = sk + L::kBytes;
+        __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
+        // S^T = K Q^T
+        f32x16 s[NKB];
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(
+                sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
+            const f32x16 zero = {};
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+          }
+        }
+
+        __builtin_amdgcn_s_setprio(0);
+        const bool masked = (CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len);
+        // visibility of accumulator element e of 32-key block kb
+        auto visible = [&](int kb, int e) {
+          const int key = k0 + 32 * kb + acc_key(e, g2);
+          return (key < len) && (!CAUSAL || key <= qrow);
+        };
+
+        uint32_t pk[NKB][8];  // bf16 pairs of P (or of silu scores)
+        if constexpr (EPI == Epilogue::Softmax) {
+          // Masked scores become -inf; with cexp > 0 (the host never passes 0)
+          // their weights exp2(-inf) are exactly 0, with no per-element select.
+          if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (!visible(kb, e)) s[kb][e] = kNegInf;
+          }
+          float mt = kNegInf;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+          mt = max_xor32(mt);
+          const float mts = mt * cexp;  // -inf stays -inf
+          if (wave_any(mts > m_ref + kRescaleSlack)) {
+            const float mn = fmaxf(m_ref, mts);
+            const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m_ref - mn);
+            m_ref = mn;
+            l_part *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDB; ++i)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[i][e] *= alpha;
+          }
+          const float nm = -m_ref;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              p[e] = exp2_hw(__builtin_fmaf(s[kb][e], cexp, nm));
+              l_part += p[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+          }
+        } else {
+          // the product is t = log2(e) alpha s (Q carries the factor):
+          // t / (1 + 2^-t) = log2(e) silu(alpha s); the factor log2(e) comes off
+          // in the epilogue's scale
+          float y[NKB][16];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float t = s[kb][e];
+              y[kb][e] = t * rcp_hw(1.f + exp2_hw(-t));
+            }
+          if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (!visible(kb, e)) y[kb][e] = 0.f;
+          }
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[kb][2 * e], y[kb][2 * e + 1]);
+        }
+
+        __builtin_amdgcn_s_setprio(1);
+        // O^T += V^T P^T; V^T fragments gathered by transposing reads
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(
-              sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
-          const f32x16 zero = {};
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
+            const bf16x8 pb = as_bf16x8(pw);
+            const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
+            const unsigned char* vrow = sv + krow * L::vRow;
+            const int swz = L::vswz(krow);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
+              const u32x2 lo = lds_read_tr16(addr);
+              const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
+              const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
+            }
+          }
         }
       }
 
       __builtin_amdgcn_s_setprio(0);
-      const bool masked = (CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len);
-      // visibility of accumulator element e of 32-key block kb
-      auto visible = [&](int kb, int e) {
-        const int key = k0 + 32 * kb + acc_key(e, g2);
-        return (key < len) && (!CAUSAL || key <= qrow);
-      };
-
-      uint32_t pk[NKB][8];  // bf16 pairs of P (or of silu scores)
-      if constexpr (EPI == Epilogue::Softmax) {
-        // Masked scores become -inf; with cexp > 0 (the host never passes 0)
-        // their weights exp2(-inf) are exactly 0, with no per-element select.
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (!visible(kb, e)) s[kb][e] = kNegInf;
-        }
-        float mt = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-        mt = max_xor32(mt);
-        const float mts = mt * cexp;  // -inf stays -inf
-        if (wave_any(mts > m_ref + kRescaleSlack)) {
-          const float mn = fmaxf(m_ref, mts);
-          const float alpha = (mn == kNegInf) ? 1.f : exp2_hw(m_ref - mn);
-          m_ref = mn;
-          l_part *= alpha;
-#pragma unroll
-          for (int i = 0; i < NDB; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][e] *= alpha;
-        }
-        const float nm = -m_ref;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            p[e] = exp2_hw(__builtin_fmaf(s[kb][e], cexp, nm));
-            l_part += p[e];
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-        }
-      } else {
-        // the product is t = log2(e) alpha s (Q carries the factor):
-        // t / (1 + 2^-t) = log2(e) silu(alpha s); the factor log2(e) comes off
-        // in the epilogue's scale
-        float y[NKB][16];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float t = s[kb][e];
-            y[kb][e] = t * rcp_hw(1.f + exp2_hw(-t));
-          }
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (!visible(kb, e)) y[kb][e] = 0.f;
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk[kb][e] = pack_bf16x2(y[kb][2 * e], y[kb][2 * e + 1]);
-      }
-
-      __builtin_amdgcn_s_setprio(1);
-      // O^T += V^T P^T; V^T fragments gathered by transposing reads
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
-          const bf16x8 pb = as_bf16x8(pw);
-          const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
-          const unsigned char* vrow = sv + krow * L::vRow;
-          const int swz = L::vswz(krow);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
-            const u32x2 lo = lds_read_tr16(addr);
-            const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
-          }
-        }
-      }
+      if (has_next) store_tile(buf ^ 1);
+      __syncthreads();
     }
 
-    __builtin_amdgcn_s_setprio(0);
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+    if (!wave_live || qrow >= len) return;
 
-  if (!wave_live || qrow >= len) return;
-
-  float scale_out;
-  if constexpr (EPI == Epilogue::Softmax) {
-    const float lt = sum_xor32(l_part);
-    scale_out = lt > 0.f ? 1.f / lt : 0.f;
-    if (a.lse != nullptr && g2 == 0) {
-      a.lse[lse_base + qrow] = lt > 0.f ? (m_ref + log2_hw(lt)) * kLn2 : kNegInf;
+    float scale_out;
+    if constexpr (EPI == Epilogue::Softmax) {
+      const float lt = sum_xor32(l_part);
+      scale_out = lt > 0.f ? 1.f / lt : 0.f;
+      if (a.lse != nullptr && g2 == 0) {
+        a.lse[lse_base + qrow] = lt > 0.f ? (m_ref + log2_hw(lt)) * kLn2 : kNegInf;
+      }
+    } else {
+      scale_out = a.inv_n * kLn2;  // the weights carry a factor log2(e)
     }
+    uint16_t* orow = op + (long)qrow * row_stride;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        u32x2 t;
+        t[0] = pack_bf16x2(acc[db][4 * jq] * scale_out, acc[db][4 * jq + 1] * scale_out);
+        t[1] = pack_bf16x2(acc[db][4 * jq + 2] * scale_out, acc[db][4 * jq + 3] * scale_out);
+        stg8(orow + 32 * db + 8 * jq + 4 * g2, t);
+      }
+  };
+
+  if (!pair) {
+    run_block(nq - 1 - slot);
   } else {
-    scale_out = a.inv_n * kLn2;  // the weights carry a factor log2(e)
+    const int nqb = (min(len, a.N) + kBM - 1) / kBM;  // query blocks of this sequence
+    const int j = nqb - 1 - slot;
+    if (slot > j) return;  // uniform over the workgroup
+    run_block(j);
+    if (j != slot) run_block(slot);  // the previous block ended with a barrier: LDS is free
   }
-  uint16_t* orow = op + (long)qrow * row_stride;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      u32x2 t;
-      t[0] = pack_bf16x2(acc[db][4 * jq] * scale_out, acc[db][4 * jq + 1] * scale_out);
-      t[1] = pack_bf16x2(acc[db][4 * jq + 2] * scale_out, acc[db][4 * jq + 3] * scale_out);
-      stg8(orow + 32 * db + 8 * jq + 4 * g2, t);
-    }
 }
 
 template <int D, bool CAUSAL, Epilogue EPI, bool JAGGED>
 hipError_t launch_one(const TileArgs& a, hipStream_t stream) {
   const int nq = (a.N + kBM - 1) / kBM;
-  const long grid = (long)nq * a.H * a.B;
+  // causal work per query block grows with its index; when the paired grid
+  // fits on the chip at once (256 CUs x resident workgroups), balance it
+  const long resident = 256L * Cfg<D>::kWavesPerSimd;
+  const int pair = (CAUSAL && (long)((nq + 1) / 2) * a.H * a.B <= resident) ? 1 : 0;
+  const long grid = (long)(pair ? (nq + 1) / 2 : nq) * a.H * a.B;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((tile_kernel<D, CAUSAL, EPI, JAGGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nq);
+  hipLaunchKernelGGL((tile_kernel<D, CAUSAL, EPI, JAGGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nq,
+                     pair);
   return hipGetLastError();
 }
 
