@@ -236,6 +236,16 @@ def test_full_prefill_d128(case):
     _full_size_check(case, [(0, 0), (3, 17), (7, 31)])
 
 
+@pytest.mark.parametrize("d,N", [(64, 1100), (128, 900)])
+def test_prefill_causal_multi_round_ragged(d, N):
+    """Causal grids too large to pair (B*H*ceil(nq/2) above the resident
+    workgroups: 1024 for d = 64, 768 for d = 128) take one query block per
+    workgroup, heaviest first; N is not a multiple of the 128-row block."""
+    _need_gpu()
+    case = W.Dense(f"prefill_multi_round_d{d}", 8, 32, 8, N, d, 1.0 / math.sqrt(d), True, "bf16", 1010 + d)
+    _full_size_check(case, [(0, 0), (5, 13), (7, 31)])
+
+
 def test_full_prefill_long_causal():
     _need_gpu()
     _full_size_check(W.PREFILL_LONG, [(0, 0), (0, 21)])
@@ -369,6 +379,22 @@ def test_hstu_small_every_element(d, causal):
     for b, r in ref.items():
         s, e = int(x.offsets[b]), int(x.offsets[b + 1])
         assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
+
+
+def test_hstu_d128_multi_round():
+    """d = 128 jagged HSTU whose grid is too large to pair (16 sequences x 4
+    heads x 16 slots > 768 resident workgroups): one query block per
+    workgroup, blocks past a sequence's end exit."""
+    _need_gpu()
+    lengths = [4096, 3000, 17, 0, 2049, 128, 1, 4000, 512, 640, 3333, 2, 1024, 4095, 100, 2500]
+    c = W.Jagged("hstu_d128_multi_round", 16, 4, 128, 1, 4096, 0.125, 1.0 / 4096, True, 43, 0.5)
+    x = W.jagged_inputs(c, lengths=lengths)
+    o = run_hstu(x, 1)
+    ref = hstu_ref(x, True, seqs=[0, 2, 3, 4, 6, 13])
+    for b, r in ref.items():
+        s0, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert_bf16(o[s0:e], r, f"seq {b} len {e - s0}")
+    assert np.isfinite(o).all()
 
 
 @pytest.mark.parametrize("causal", [0, 1])
