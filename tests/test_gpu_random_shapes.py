@@ -1,5 +1,6 @@
 """Seeded random-shape parity sweep of every entry point against the fp64
-oracle: each case draws its own shape (batch, heads, group size, sequence
+oracle (prefill, decode contiguous and paged, jagged HSTU, backward, FP8
+prefill): each case draws its own shape (batch, heads, group size, sequence
 length, head dim, causal flag, scale; decode lengths including 0 and Lmax,
 split counts, page sizes; jagged lengths including empty sequences) and is
 compared on every output element.  The case parameters are in the test id and
@@ -157,3 +158,74 @@ def test_random_hstu(i):
         ref = oracle.hstu_jagged(bf16_bits_to_f64(x.q[s:e]), bf16_bits_to_f64(x.k[s:e]), bf16_bits_to_f64(x.v[s:e]),
                                  sub, jc.alpha, jc.inv_n, bool(c["causal"]))
         assert_bf16(got[s:e], ref, f"seq {b} " + str(c))
+
+
+def _bwd_case(i):
+    r = np.random.default_rng(np.random.SeedSequence([7004, i]))
+    d = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4]))
+    Hkv = int(r.integers(1, 3))
+    B = int(r.integers(1, 3))
+    N = int(r.integers(1, 12)) if r.random() < 0.3 else int(r.integers(60, 400))
+    causal = int(r.integers(0, 2))
+    scale = float(1 / math.sqrt(d)) if r.random() < 0.5 else float(r.uniform(0.02, 0.2))
+    return dict(B=B, H=G * Hkv, Hkv=Hkv, N=N, d=d, causal=causal, scale=scale, seed=7400 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_backward(i):
+    _need_gpu()
+    from synthgen import TENSOR_DO
+
+    from _util import assert_grad
+
+    c = _bwd_case(i)
+    B, H, Hkv, N, d = c["B"], c["H"], c["Hkv"], c["N"], c["d"]
+    q = normal_bf16(c["seed"], TENSOR_Q, (B, H, N, d))
+    k = normal_bf16(c["seed"], TENSOR_K, (B, Hkv, N, d))
+    v = normal_bf16(c["seed"], TENSOR_V, (B, Hkv, N, d))
+    do = normal_bf16(c["seed"], TENSOR_DO, (B, H, N, d))
+    tq, tk, tv, tdo = (to_dev_bf16(x) for x in (q, k, v, do))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.attn_fwd(tq, tk, tv, o, lse, B, H, Hkv, N, d, c["scale"], c["causal"])
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    nbytes = fa.attn_bwd_workspace_bytes(B, H, N)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, B, H, Hkv, N, d, c["scale"], c["causal"], ws, nbytes)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v),
+                                           bf16_bits_to_f64(do), c["scale"], bool(c["causal"]))
+    assert_grad(bf16_dev_to_f64(dq), rq, "dQ " + str(c))
+    assert_grad(bf16_dev_to_f64(dk), rk, "dK " + str(c))
+    assert_grad(bf16_dev_to_f64(dv), rv, "dV " + str(c))
+
+
+def _fp8_case(i):
+    r = np.random.default_rng(np.random.SeedSequence([7005, i]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.integers(1, 3))
+    B = int(r.integers(1, 3))
+    N = int(r.integers(1, 12)) if r.random() < 0.3 else int(r.integers(60, 500))
+    causal = int(r.integers(0, 2))
+    return dict(B=B, H=G * Hkv, Hkv=Hkv, N=N, causal=causal, seed=7500 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_fp8(i):
+    _need_gpu()
+    from _util import assert_fp8
+
+    c = _fp8_case(i)
+    dc = W.Dense("random_fp8", c["B"], c["H"], c["Hkv"], c["N"], 128, 1 / math.sqrt(128), bool(c["causal"]), "fp8",
+                 c["seed"])
+    x = W.fp8_dense_inputs(dc)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    o = torch.empty((dc.B, dc.H, dc.N, dc.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((dc.B, dc.H, dc.N), dtype=torch.float32, device="cuda")
+    fa.attn_fwd_fp8(t(x.q), t(x.k), t(x.v), o, lse, t(x.descale_q), t(x.descale_k), t(x.descale_v), dc.B, dc.H,
+                    dc.Hkv, dc.N, dc.d, dc.scale, int(dc.causal))
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_forward(x.f64("q"), x.f64("k"), x.f64("v"), dc.scale, bool(dc.causal))
+    assert_fp8(bf16_dev_to_f64(o), O_ref, str(c))
+    assert_lse(lse.cpu().numpy(), L_ref, str(c))
