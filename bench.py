@@ -243,7 +243,20 @@ def cpu_baseline(x, case, seconds: float):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (b,h) heads of the B={case.B} H={case.H} N={case.N} d={case.d} "
                   f"{'causal' if case.causal else 'non-causal'} prefill, all rows, fp64 numpy, {el:.1f} s",
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _time_calls(fn, stream, warmup: int = 3, reps: int = 10) -> float:
