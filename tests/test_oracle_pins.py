@@ -346,3 +346,68 @@ def test_bf16_rounding_is_nearest_even():
     r = np.random.default_rng(66).standard_normal(100000).astype(np.float32) * 10
     assert np.array_equal(bf16_bits_to_f64(f32_to_bf16_bits(r)),
                           torch.from_numpy(r).to(torch.bfloat16).to(torch.float64).numpy())
+
+
+# --- brute force in extended precision ---------------------------------------
+
+def _brute_attention(q, k, v, scale, causal):
+    """Nested loops in extended precision, written from the definition:
+    s_ij = scale q_i.k_j over visible j, m_i = max, l_i = sum exp(s - m),
+    O_i = sum exp(s - m) v_j / l_i, LSE_i = m_i + ln l_i."""
+    ld = np.longdouble
+    n, d = q.shape
+    O = np.zeros((n, v.shape[1]), dtype=ld)
+    L = np.zeros(n, dtype=ld)
+    for i in range(n):
+        js = list(range(i + 1)) if causal else list(range(k.shape[0]))
+        s = []
+        for j in js:
+            acc = ld(0)
+            for c in range(d):
+                acc += ld(q[i, c]) * ld(k[j, c])
+            s.append(ld(scale) * acc)
+        m = max(s)
+        w = [np.exp(x - m) for x in s]
+        tot = sum(w)
+        for t, j in enumerate(js):
+            for c in range(v.shape[1]):
+                O[i, c] += w[t] / tot * ld(v[j, c])
+        L[i] = m + np.log(tot)
+    return O, L
+
+
+@pytest.mark.parametrize("n", [1, 5, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_matches_extended_precision_brute_force(n, causal):
+    q, k, v = rnd(90 + n, n, 8), rnd(91 + n, n, 8), rnd(92 + n, n, 6)
+    scale = 0.37
+    O, L = oracle.attention_forward(q[None, None], k[None, None], v[None, None], scale, causal)
+    Ob, Lb = _brute_attention(q, k, v, scale, causal)
+    np.testing.assert_allclose(O[0, 0], Ob.astype(np.float64), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L[0, 0], Lb.astype(np.float64), rtol=0, atol=1e-13)
+
+
+def _brute_hstu(q, k, v, alpha, inv_n, causal):
+    """HSTU in extended precision with loops: x = alpha q_i.k_j,
+    y = x / (1 + e^-x) over visible j, O_i = inv_n sum y v_j."""
+    ld = np.longdouble
+    n, d = q.shape
+    O = np.zeros((n, v.shape[1]), dtype=ld)
+    for i in range(n):
+        for j in (range(i + 1) if causal else range(n)):
+            x = ld(0)
+            for c in range(d):
+                x += ld(q[i, c]) * ld(k[j, c])
+            x *= ld(alpha)
+            y = x / (ld(1) + np.exp(-x))
+            for c in range(v.shape[1]):
+                O[i, c] += ld(inv_n) * y * ld(v[j, c])
+    return O
+
+
+@pytest.mark.parametrize("n", [1, 6, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_hstu_matches_extended_precision_brute_force(n, causal):
+    q, k, v = rnd(93 + n, n, 8), rnd(94 + n, n, 8), rnd(95 + n, n, 5)
+    O = oracle.hstu_dense(q, k, v, 0.6, 0.125, causal)
+    np.testing.assert_allclose(O, _brute_hstu(q, k, v, 0.6, 0.125, causal).astype(np.float64), rtol=0, atol=1e-14)
