@@ -74,7 +74,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements after the timed step (other prefill shapes, decode "
-                         "split sweep, GPU clock and power)")
+                         "split sweep)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -276,53 +276,9 @@ def _time_calls(fn, stream, warmup: int = 3, reps: int = 10) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def _sample_clock_and_power(keep_busy, seconds: float = 4.0):
-    """GPU clock (MHz, mean over the XCDs) and socket power (W) read by amd-smi
-    while a second thread keeps launching keep_busy(); None if amd-smi is
-    missing or its output cannot be read."""
-    import shutil
-    import subprocess
-    import threading
-
-    import torch
-
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return None
-    stop = threading.Event()
-
-    def launcher():
-        t_end = time.perf_counter() + seconds
-        while not stop.is_set() and time.perf_counter() < t_end:
-            keep_busy()
-
-    th = threading.Thread(target=launcher)
-    th.start()
-    try:
-        time.sleep(0.5)  # let the queue fill and the clock settle
-        r = subprocess.run([exe, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=30)
-    finally:
-        stop.set()
-        th.join()
-        torch.cuda.synchronize()
-    try:
-        data = json.loads(r.stdout)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clocks = [c["clk"]["value"] for name, c in gpu["clock"].items()
-                  if name.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
-                  and isinstance(c["clk"].get("value"), (int, float))]
-        power = gpu["power"]["socket_power"]["value"]
-        return {"gfx_mhz": round(sum(clocks) / len(clocks), 1) if clocks else None,
-                "socket_power_w": power if isinstance(power, (int, float)) else None,
-                "source": "amd-smi metric -c -p, sampled while the headline prefill runs"}
-    except (ValueError, KeyError, IndexError, TypeError):
-        return None
-
-
-def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl, do, dlse,
-                         headline_tflops):
-    """Other prefill shapes, a decode split sweep and the GPU clock under the
-    headline prefill, each timed with HIP events after the timed step."""
+def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl, do, dlse):
+    """Other prefill shapes and a decode split sweep, each timed with HIP events
+    after the timed step."""
     import torch
 
     ctx = {}
@@ -355,13 +311,6 @@ def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, 
                                                   dc.scale, sp, ws, wsb), stream, reps=20)
         sweep[str(sp)] = {"GB/s": round(nbytes / (ms_d * 1e-3) / 1e9, 1), "ms_per_call": round(ms_d, 4)}
     ctx["decode_splits"] = sweep
-    # GPU clock and power under the headline prefill
-    cp = _sample_clock_and_power(lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 1))
-    if cp is not None and cp.get("gfx_mhz"):
-        peak_at_clk = PEAK_BF16_TFLOPS * cp["gfx_mhz"] / 2400.0
-        cp["prefill_peak_at_gfx_clock"] = round(peak_at_clk, 1)
-        cp["prefill_frac_at_gfx_clock"] = round(headline_tflops / peak_at_clk, 4)
-    ctx["clock_under_prefill"] = cp
     return ctx
 
 
@@ -604,7 +553,7 @@ def main(argv=None) -> int:
     if not args.only and not args.no_context:
         print("bench: context measurements", file=sys.stderr, flush=True)
         out["context"] = context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl,
-                                              do, dlse, out["roofline"]["achieved"])
+                                              do, dlse)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(px, pc, args.cpu_seconds)

@@ -63,10 +63,17 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 // while some of them are in the softmax.
 template <int D>
 struct Cfg;
+//
+// kKAhead / kVAhead: LDS operand reads kept in flight ahead of the products
+// (K fragments of the score product, V^T fragments of the PV product), as many
+// as the register budget leaves room for; 0 leaves the order to the compiler
+// (measured faster for d = 64, whose four waves per SIMD hide the latency).
 template <>
 struct Cfg<128> {
   static constexpr int BN = 32;
   static constexpr int kWavesPerSimd = 3;
+  static constexpr int kKAhead = 3;
+  static constexpr int kVAhead = 3;
 };
 template <>
 struct Cfg<256> {
@@ -75,11 +82,15 @@ struct Cfg<256> {
   // accumulators in the AGPR half of the register file
   static constexpr int BN = 32;
   static constexpr int kWavesPerSimd = 1;
+  static constexpr int kKAhead = 3;
+  static constexpr int kVAhead = 3;
 };
 template <>
 struct Cfg<64> {
   static constexpr int BN = 64;
   static constexpr int kWavesPerSimd = 4;
+  static constexpr int kKAhead = 0;
+  static constexpr int kVAhead = 0;
 };
 
 template <int D, int BN>
@@ -260,14 +271,38 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
         __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
         // S^T = K Q^T
         f32x16 s[NKB];
+        auto kread = [&](int c, int kb) {
+          return *reinterpret_cast<const u32x4*>(sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
+        };
+        if constexpr (Cfg<D>::kKAhead == 0) {
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) {
+          for (int c = 0; c < NDC; ++c)
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
+            for (int kb = 0; kb < NKB; ++kb) {
+              const f32x16 zero = {};
+              s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kread(c, kb)), qf[c], c == 0 ? zero : s[kb], 0,
+                                                              0, 0);
+            }
+        } else {
+          // each K fragment read KW products ahead of its use; the schedule is
+          // pinned: KW reads, then one product and one read at a time
+          constexpr int SSTEPS = NDC * NKB;
+          constexpr int KW = Cfg<D>::kKAhead < SSTEPS ? Cfg<D>::kKAhead : SSTEPS;
+          u32x4 kf[SSTEPS];
+#pragma unroll
+          for (int t = 0; t < KW; ++t) kf[t] = kread(t / NKB, t % NKB);
+#pragma unroll
+          for (int t = 0; t < SSTEPS; ++t) {
+            const int c = t / NKB, kb = t % NKB;
             const f32x16 zero = {};
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), qf[c], c == 0 ? zero : s[kb], 0, 0, 0);
+            if (t + KW < SSTEPS) kf[t + KW] = kread((t + KW) / NKB, (t + KW) % NKB);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);  // DS reads
+#pragma unroll
+          for (int t = 0; t < SSTEPS; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (t + KW < SSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
         }
 
@@ -346,23 +381,45 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
 
         __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T; V^T fragments gathered by transposing reads
+        auto vread = [&](int kb, int jj, int db) {
+          const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
+          const unsigned char* addr = sv + krow * L::vRow + (((4 * db + tr_chunk) ^ L::vswz(krow)) << 4) + tr_byte;
+          const u32x2 lo = lds_read_tr16(addr);
+          const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        auto pfrag = [&](int kb, int jj) {
+          const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
+          return as_bf16x8(pw);
+        };
+        if constexpr (Cfg<D>::kVAhead == 0) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
-            const bf16x8 pb = as_bf16x8(pw);
-            const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
-            const unsigned char* vrow = sv + krow * L::vRow;
-            const int swz = L::vswz(krow);
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
-              const u32x2 lo = lds_read_tr16(addr);
-              const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
-              const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), pb, acc[db], 0, 0, 0);
-            }
+              for (int db = 0; db < NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vread(kb, jj, db)), pfrag(kb, jj), acc[db],
+                                                                  0, 0, 0);
+        } else {
+          // each V^T fragment read PW products ahead of its use (pinned as above)
+          constexpr int PSTEPS = NKB * 2 * NDB;
+          constexpr int PW = Cfg<D>::kVAhead < PSTEPS ? Cfg<D>::kVAhead : PSTEPS;
+          u32x4 vfr[PSTEPS];
+          auto vstep = [&](int t) { return vread(t / (2 * NDB), (t / NDB) % 2, t % NDB); };
+#pragma unroll
+          for (int t = 0; t < PW; ++t) vfr[t] = vstep(t);
+#pragma unroll
+          for (int t = 0; t < PSTEPS; ++t) {
+            const int kb = t / (2 * NDB), jj = (t / NDB) % 2, db = t % NDB;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr[t]), pfrag(kb, jj), acc[db], 0, 0, 0);
+            if (t + PW < PSTEPS) vfr[t + PW] = vstep(t + PW);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * PW, 1);
+#pragma unroll
+          for (int t = 0; t < PSTEPS; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (t + PW < PSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
           }
         }
       }
