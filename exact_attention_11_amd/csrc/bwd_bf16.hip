@@ -382,15 +382,31 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
     // are 8 consecutive queries (the B operand of the second product)
     const unsigned char* sa = first ? sq : sdo;
     f32x16 s[2];
+    // each A fragment is read KW products ahead of its use; the order is
+    // pinned (KW reads, then one product and one read at a time) so that the
+    // products do not wait on LDS latency
+    constexpr int SSTEPS = 2 * NDC;
+    constexpr int KW = 2;
+    u32x4 af[SSTEPS];
+    auto aread = [&](int t) {
+      const int c = t / 2, mb = t % 2;
+      const int qr = 32 * mb + key_perm(n32);
+      return *reinterpret_cast<const u32x4*>(sa + qr * ROW + (((2 * c + g2) ^ swz_kv<D>(qr)) << 4));
+    };
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int t = 0; t < KW; ++t) af[t] = aread(t);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int qr = 32 * mb + key_perm(n32);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(sa + qr * ROW + (((2 * c + g2) ^ swz_kv<D>(qr)) << 4));
-        const f32x16 zero = {};
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x), bop[c], c == 0 ? zero : s[mb], 0, 0, 0);
-      }
+    for (int t = 0; t < SSTEPS; ++t) {
+      const int c = t / 2, mb = t % 2;
+      const f32x16 zero = {};
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[t]), bop[c], c == 0 ? zero : s[mb], 0, 0, 0);
+      if (t + KW < SSTEPS) af[t + KW] = aread(t + KW);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
+#pragma unroll
+    for (int t = 0; t < SSTEPS; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + KW < SSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 
     __builtin_amdgcn_s_setprio(0);
@@ -444,21 +460,32 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
     // dV^T += dO^T P (first wave) or dK^T += Q^T dS (second wave); dO^T and
     // Q^T gathered by transposing reads
     const unsigned char* sb = first ? sdo : sq;
+    // fragments read PW products ahead, pinned as above
+    constexpr int PSTEPS = 4 * NDB;
+    constexpr int PW = 2;
+    u32x4 bt[PSTEPS];
+    auto bread = [&](int t) {
+      const int mb = t / (2 * NDB), jj = (t / NDB) % 2, db = t % NDB;
+      const int qrow = 32 * mb + 16 * jj + 8 * g2 + tr_row;
+      const int ch = 4 * db + tr_chunk;
+      const u32x2 lo = lds_read_tr16(sb + qrow * ROW + ((ch ^ swz_kv<D>(qrow)) << 4) + tr_byte);
+      const u32x2 hi = lds_read_tr16(sb + (qrow + 4) * ROW + ((ch ^ swz_kv<D>(qrow + 4)) << 4) + tr_byte);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int t = 0; t < PW; ++t) bt[t] = bread(t);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const u32x4 pw = {w[mb][4 * jj], w[mb][4 * jj + 1], w[mb][4 * jj + 2], w[mb][4 * jj + 3]};
-        const int qrow = 32 * mb + 16 * jj + 8 * g2 + tr_row;
+    for (int t = 0; t < PSTEPS; ++t) {
+      const int mb = t / (2 * NDB), jj = (t / NDB) % 2, db = t % NDB;
+      const u32x4 pw = {w[mb][4 * jj], w[mb][4 * jj + 1], w[mb][4 * jj + 2], w[mb][4 * jj + 3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bt[t]), as_bf16x8(pw), acc[db], 0, 0, 0);
+      if (t + PW < PSTEPS) bt[t + PW] = bread(t + PW);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PW, 1);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int ch = 4 * db + tr_chunk;
-          const u32x2 lo = lds_read_tr16(sb + qrow * ROW + ((ch ^ swz_kv<D>(qrow)) << 4) + tr_byte);
-          const u32x2 hi = lds_read_tr16(sb + (qrow + 4) * ROW + ((ch ^ swz_kv<D>(qrow + 4)) << 4) + tr_byte);
-          const u32x4 at = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(at), as_bf16x8(pw), acc[db], 0, 0, 0);
-        }
-      }
+    for (int t = 0; t < PSTEPS; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (t + PW < PSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
     __builtin_amdgcn_s_setprio(0);
   }
