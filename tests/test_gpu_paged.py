@@ -105,3 +105,27 @@ def test_full_paged_decode_gqa(P):
     O_ref, L_ref = paged_ref(px)
     assert_bf16(bf16_dev_to_f64(o), O_ref, f"paged P={P}")
     assert_lse(lse.cpu().numpy(), L_ref, f"paged P={P}")
+
+
+def test_paged_clamps_table_entries_and_lengths():
+    """Block-table entries are clamped to [0, num_pages) and lengths to
+    [0, max_pages_per_seq * page_size] on the device: an entry past the pool
+    reads the pool's last page, a negative one page 0, and a length past the
+    table the whole table."""
+    _need_gpu()
+    P = 64
+    c = W.Decode("paged_clamp", 3, 8, 2, 704, 128, 1 / math.sqrt(128), 1, 704, 52)
+    x = W.decode_inputs(c, seqlens=[704, 300, 704])
+    px = W.paged_from_decode(x, P, spare_pages=0, perm_seed=9)
+    O_ref, L_ref = paged_ref(px)
+    last = px.num_pages - 1
+    table = px.block_table.copy()
+    ib, ip = np.argwhere(table == last)[0]
+    jb, jp = np.argwhere(table == 0)[0]
+    table[ib, ip] = last + 1000
+    table[jb, jp] = -3
+    x.seqlens[:] = [704 + 77, 300, 704 + 5000]
+    bad = W.PagedDecodeInputs(x, P, px.k_pages, px.v_pages, table, px.num_pages)
+    o, lse = run_paged(bad, 0)
+    assert_bf16(bf16_dev_to_f64(o), O_ref, "clamped table and lengths")
+    assert_lse(lse.cpu().numpy(), L_ref, "clamped table and lengths")

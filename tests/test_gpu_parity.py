@@ -438,3 +438,45 @@ def test_full_hstu_jagged():
     for b, r in ref.items():
         s, e = int(x.offsets[b]), int(x.offsets[b + 1])
         assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
+
+
+def test_decode_clamps_lengths_to_the_cache():
+    """seqlens_k is read only on the device and clamped to [0, Lmax]: a length
+    past the cache gives the full-cache result, a negative one the empty
+    result (O = 0, LSE = -inf), and nothing outside the cache is read."""
+    _need_gpu()
+    c = W.Decode("decode_clamp", 4, 8, 2, 700, 128, 1 / math.sqrt(128), 1, 700, 34)
+    x = W.decode_inputs(c, seqlens=[700, 0, 0, 700])
+    x.seqlens[:] = [700 + 500, -7, 0, 700]
+    o, lse = run_decode(x, 0)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert np.all(o[2] == 0) and np.all(np.isneginf(lse[2]))
+    x.seqlens[:] = [700, 0, 0, 700]
+    O_ref, L_ref = decode_ref(x, [0, 3])
+    assert_bf16(o[[0, 3]], O_ref)
+    assert_lse(lse[[0, 3]], L_ref)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_hstu_rows_past_max_seqlen_are_not_computed(causal):
+    """A sequence longer than max_seqlen (a violated precondition) is cut to
+    its first max_seqlen rows and keys: those rows match the oracle on the cut
+    sequence, the rows past it are left as they were (NaN here), and nothing
+    is read outside the sequence."""
+    _need_gpu()
+    c = W.Jagged("hstu_clamp", 3, 2, 64, 1, 300, 0.25, 1.0 / 64, bool(causal), 44, 1.0)
+    x = W.jagged_inputs(c, lengths=[300, 50, 130])
+    T = int(x.offsets[-1])
+    q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
+    off = to_dev(x.offsets)
+    o = torch.full((T, c.H, c.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fa.attn_hstu_jagged(q, k, v, o, off, 3, c.H, c.d, 200, c.alpha, c.inv_n, causal)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(o)
+    for b, keep in ((0, 200), (1, 50), (2, 130)):
+        s = int(x.offsets[b])
+        sub = np.array([0, keep], dtype=np.int64)
+        ref = oracle.hstu_jagged(bf16_bits_to_f64(x.q[s:s + keep]), bf16_bits_to_f64(x.k[s:s + keep]),
+                                 bf16_bits_to_f64(x.v[s:s + keep]), sub, c.alpha, c.inv_n, bool(causal))
+        assert_bf16(got[s:s + keep], ref, f"seq {b}")
+    assert np.isnan(got[200:300]).all()
