@@ -82,13 +82,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
-  // (batch, head, query block), heaviest blocks first, all blocks of a head
-  // on one XCD (dispatch is round-robin over 8 XCDs)
-  const int G = gridDim.x;
-  int wid = blockIdx.x;
-  if ((G & 7) == 0) wid = (wid & 7) * (G >> 3) + (wid >> 3);
-  const int qb = nq - 1 - (wid % nq);
-  const int bh = wid / nq;
+  // (batch, head, query block): all blocks of a head on one XCD, heads taken
+  // four at a time, heaviest blocks of a group first
+  int slot, bh;
+  grouped_item(a.B * a.H, nq, 4, bh, slot);
+  const int qb = nq - 1 - slot;
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int g = h / (a.H / a.Hkv);
@@ -280,12 +278,11 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
   const int g2 = lane >> 5;
 
   // (batch, kv-head, key block); the first key blocks carry the most causal
-  // work and go first; all blocks of a kv-head on one XCD
-  const int Gd = gridDim.x;
-  int wid = blockIdx.x;
-  if ((Gd & 7) == 0) wid = (wid & 7) * (Gd >> 3) + (wid >> 3);
-  const int kblk = wid % nkb;
-  const int bg = wid / nkb;
+  // work: all blocks of a kv-head on one XCD, kv-heads taken four at a time,
+  // first key blocks of a group first (with the dQ kernel's grouping, the
+  // backward measured ~3 % faster than one head at a time)
+  int kblk, bg;
+  grouped_item(a.B * a.Hkv, nkb, 4, bg, kblk);
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int N = a.N;

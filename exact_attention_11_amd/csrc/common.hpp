@@ -120,4 +120,29 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
+// Work item of this workgroup in a grid of nheads x nblk items, block 0 the
+// heaviest.  Dispatch is round-robin over the 8 XCDs in blockIdx order; when
+// the grid and the head count divide by 8, each XCD gets its own heads (their
+// K/V stay in its L2), takes them `group` at a time and dispatches the
+// heaviest blocks of a group first, so the launch ends with light blocks.
+// Otherwise items go head by head, heaviest block first, consecutive items on
+// one XCD when the grid divides by 8.
+__device__ __forceinline__ void grouped_item(int nheads, int nblk, int group, int& head, int& blk) {
+  const int G = gridDim.x;
+  int w = blockIdx.x;
+  if ((G & 7) == 0 && (nheads & 7) == 0) {
+    const int hx = nheads >> 3;  // heads of each XCD
+    const int u = w >> 3;        // dispatch rank within the XCD
+    const int gi = u / (group * nblk);
+    const int gs = min(group, hx - gi * group);  // heads in this group
+    const int within = u - gi * group * nblk;
+    blk = within / gs;
+    head = (w & 7) * hx + gi * group + within % gs;
+  } else {
+    if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+    blk = w % nblk;
+    head = w / nblk;
+  }
+}
+
 }  // namespace fattn

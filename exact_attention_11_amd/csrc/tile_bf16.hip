@@ -143,35 +143,15 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
-  // ---- work item: (batch, head, slot), all slots of a head on one XCD
-  // (dispatch is round-robin over 8 XCDs, in blockIdx order).  Unpaired:
-  // slot = one query block; each XCD takes its heads kHeadGroup at a time and
-  // dispatches the heaviest query blocks of a group first, so the last
-  // workgroups of the launch are light ones while only a few heads' K/V are
-  // live in the XCD's L2 (the dispatch order alone left a ~10 % tail).  Paired (causal grids that fit on the chip at once):
-  // slot i runs query blocks nqb-1-i and i, so every workgroup does the same
-  // work and no CU is left with the heaviest blocks.
-  const int G = gridDim.x;
+  // ---- work item: (batch, head, slot), all slots of a head on one XCD.
+  // Unpaired: slot = one query block; each XCD takes its heads kHeadGroup at
+  // a time, heaviest query blocks of a group first (one head at a time left a
+  // ~10 % tail of heavy blocks started late).  Paired (causal grids that fit
+  // on the chip at once): slot i runs query blocks nqb-1-i and i, so every
+  // workgroup does the same work and no CU is left with the heaviest blocks.
   const int nslot = pair ? (nq + 1) / 2 : nq;
   int slot, bh;
-  if ((G & 7) == 0 && ((a.B * a.H) & 7) == 0) {
-    const int hx = a.B * a.H / 8;  // heads of each XCD
-    const int u = blockIdx.x >> 3;  // dispatch rank within the XCD
-    if (pair) {
-      slot = u % nslot;
-      bh = (blockIdx.x & 7) * hx + u / nslot;
-    } else {
-      constexpr int HG = Cfg<D>::kHeadGroup;
-      const int gi = u / (HG * nslot);
-      const int gs = min(HG, hx - gi * HG);  // heads in this group
-      const int within = u - gi * HG * nslot;
-      slot = within / gs;
-      bh = (blockIdx.x & 7) * hx + gi * HG + within % gs;
-    }
-  } else {
-    slot = blockIdx.x % nslot;
-    bh = blockIdx.x / nslot;
-  }
+  grouped_item(a.B * a.H, nslot, pair ? 1 : Cfg<D>::kHeadGroup, bh, slot);
   const int h = bh % a.H;
   const int b = bh / a.H;
 
