@@ -326,8 +326,8 @@ def main(argv=None) -> int:
         traffic_summary(*args.traffic, kernels=args.traffic_kernel)
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is described "
-              "in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the kernels are measured on one GPU's "
+              "share at its real shape; sharding over several GPUs is not built.", file=sys.stderr)
         return 2
 
     import numpy as np
