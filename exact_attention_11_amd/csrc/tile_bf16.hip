@@ -38,7 +38,8 @@
 //    (HSTU page, the listing and optimisation one).  Q is multiplied by
 //    alpha*log2(e) as it is loaded, so the product is t = log2(e) alpha s and
 //    a weight is t / (1 + 2^-t) = log2(e) silu(alpha s); the epilogue's 1/n
-//    takes the factor ln 2.
+//    takes the factor ln 2.  (d = 128; the d = 64 HSTU kernel at the end of
+//    this file splits each query block's keys between two wave pairs.)
 //
 // Causal masking is generated in the kernel from tile positions: tiles wholly
 // below the diagonal run unmasked, tiles straddling it are masked per element,
@@ -493,6 +494,200 @@ hipError_t launch_causal(const TileArgs& a, hipStream_t s) {
   return a.causal ? launch_one<D, true, EPI, JAGGED>(a, s) : launch_one<D, false, EPI, JAGGED>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Jagged HSTU, d = 64: the key tiles of each query block are split between two
+// pairs of waves.  A workgroup owns 64 query rows; wave w takes rows
+// 32 (w & 1) .. +32 and the key tiles of parity w >> 1, so the longest chain of
+// a launch (the last query block of the longest sequence) walks half the keys
+// it would with one wave per row group.  The two partial sums of a row group
+// (plain sums: the SiLU weights are not normalised) meet in LDS in a fixed
+// order at the end, so results do not depend on timing; with the tiles split
+// by parity, zero-padded keys past a sequence only add exact zeros to either
+// sum, so a zero-padded batch gives the jagged result bit for bit.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int nqb) {
+  constexpr int D = 64;
+  constexpr int BN = 32;
+  constexpr int BMW = 64;      // query rows per workgroup
+  constexpr int NDB = D / 32;  // 32-row blocks of d
+  constexpr int NDC = D / 16;  // K=16 steps over d
+  using L = Lds<D, BN>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * L::stage];  // 2 key halves x 2 stages
+  static_assert(4 * L::stage >= 2 * NDB * 16 * 64 * 4 * 2, "room for the partial sums");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wv & 1;   // row group
+  const int ks = wv >> 1;  // key half
+  const int n32 = lane & 31;
+  const int g2 = lane >> 5;
+
+  int slot, bh;
+  grouped_item(a.B * a.H, nqb, 4, bh, slot);
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int s0 = a.offsets[b];
+  const int len = min(a.offsets[b + 1] - s0, a.N);
+  const int q0 = (nqb - 1 - slot) * BMW;  // heaviest blocks first
+  if (q0 >= len) return;                  // uniform over the workgroup
+  const long rs = (long)a.H * D;           // elements between consecutive rows
+  const long base = ((long)s0 * a.H + h) * D;
+  const uint16_t* qp = (const uint16_t*)a.q + base;
+  const uint16_t* kp = (const uint16_t*)a.k + base;
+  const uint16_t* vp = (const uint16_t*)a.v + base;
+  uint16_t* op = (uint16_t*)a.o + base;
+
+  const int kv_end = CAUSAL ? min(len, q0 + BMW) : len;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const int steps = (n_tiles + 1) / 2;  // step t: tile 2t (even half) and 2t+1 (odd half)
+  const int q0w = q0 + 32 * rg;
+  const bool wave_live = q0w < len;
+  const int qrow = q0w + n32;
+
+  // Q fragments, scaled by alpha log2(e) as in the tile kernel
+  bf16x8 qf[NDC];
+  const float beta = a.c * kLog2e;
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (qrow < len) t = ldg16(qp + (long)qrow * rs + 16 * c + 8 * g2);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
+    qf[c] = as_bf16x8(t);
+  }
+
+  // step t loads tiles 2t and 2t+1: one 16-byte chunk of K and of V per
+  // thread and tile
+  const uint32_t row_bytes = (uint32_t)rs * 2;
+  const int lrow = tid >> 3, lch = tid & 7;
+  const uint32_t goff = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16u;
+  u32x4 kr[2], vr[2];
+  auto load_step = [&](int t) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int ti = 2 * t + st;
+      const int k0 = ti * BN;
+      const uint32_t bytes = (ti < n_tiles && k0 < len) ? (uint32_t)(len - k0 - 1) * row_bytes + D * 2 : 0u;
+      kr[st] = buf_load16(make_rsrc(kp + (long)(bytes ? k0 : 0) * rs, bytes), goff);
+      vr[st] = buf_load16(make_rsrc(vp + (long)(bytes ? k0 : 0) * rs, bytes), goff);
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      unsigned char* sk = smem + (st * 2 + buf) * L::stage;
+      unsigned char* sv = sk + L::kBytes;
+      *reinterpret_cast<u32x4*>(sk + lrow * L::kRow + lch * 16) = kr[st];
+      *reinterpret_cast<u32x4*>(sv + lrow * L::vRow + ((lch ^ L::vswz(lrow)) << 4)) = vr[st];
+    }
+  };
+
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  for (int t = 0; t < steps; ++t) {
+    const int buf = t & 1;
+    const bool has_next = t + 1 < steps;
+    if (has_next) load_step(t + 1);
+    const int ti = 2 * t + ks;
+    const int k0 = ti * BN;
+    const bool active = wave_live && ti < n_tiles && !(CAUSAL && k0 > q0w + 31);
+    if (active) {
+      const unsigned char* sk = smem + (ks * 2 + buf) * L::stage;
+      const unsigned char* sv = sk + L::kBytes;
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 s;
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + key_perm(n32) * L::kRow + (16 * c + 8 * g2) * 2);
+        const f32x16 zero = {};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s, 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // t / (1 + 2^-t) = log2(e) silu(alpha s); masked keys weigh 0
+      float y[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[e] = s[e] * rcp_hw(1.f + exp2_hw(-s[e]));
+      if ((CAUSAL && k0 + BN - 1 > q0w) || (k0 + BN > len)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + acc_key(e, g2);
+          if (!((key < len) && (!CAUSAL || key <= qrow))) y[e] = 0.f;
+        }
+      }
+      uint32_t pk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 pw = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
+        const int krow = 16 * jj + 8 * g2 + tr_row;
+        const unsigned char* vrow = sv + krow * L::vRow;
+        const int swz = L::vswz(krow);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
+          const u32x2 lo = lds_read_tr16(addr);
+          const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pw), acc[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (has_next) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // the odd-tile waves hand their partial sums to the even-tile waves (same
+  // lane layout)
+  float* red = reinterpret_cast<float*>(smem) + rg * (NDB * 16 * 64);
+  if (ks == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(db * 16 + e) * 64 + lane] = acc[db][e];
+  }
+  __syncthreads();
+  if (ks == 1 || !wave_live || qrow >= len) return;
+  const float scale_out = a.inv_n * kLn2;  // the weights carry a factor log2(e)
+  uint16_t* orow = op + (long)qrow * rs;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      float v4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v4[r] = (acc[db][4 * jq + r] + red[(db * 16 + 4 * jq + r) * 64 + lane]) * scale_out;
+      u32x2 t;
+      t[0] = pack_bf16x2(v4[0], v4[1]);
+      t[1] = pack_bf16x2(v4[2], v4[3]);
+      stg8(orow + 32 * db + 8 * jq + 4 * g2, t);
+    }
+}
+
+template <bool CAUSAL>
+hipError_t launch_hstu_split(const TileArgs& a, hipStream_t stream) {
+  const int nqb = (a.N + 63) / 64;
+  const long grid = (long)nqb * a.H * a.B;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((hstu_split_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nqb);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_tile_bf16(const TileArgs& a, hipStream_t stream) {
@@ -502,7 +697,7 @@ hipError_t launch_tile_bf16(const TileArgs& a, hipStream_t stream) {
     if (a.d == 256) return launch_causal<256, Epilogue::Softmax, false>(a, stream);
   } else {
     if (a.d == 128) return launch_causal<128, Epilogue::Silu, true>(a, stream);
-    if (a.d == 64) return launch_causal<64, Epilogue::Silu, true>(a, stream);
+    if (a.d == 64) return a.causal ? launch_hstu_split<true>(a, stream) : launch_hstu_split<false>(a, stream);
   }
   return hipErrorInvalidValue;
 }
