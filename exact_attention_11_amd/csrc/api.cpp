@@ -169,7 +169,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
     if (lmax_hint < 1) return 0;
     s = fattn::decode_auto_splits(B, Hkv, lmax_hint);
   }
-  const size_t bytes = (size_t)B * H * s * ((size_t)d + 1) * sizeof(float);
+  const size_t bytes = (size_t)H * B * (s + 1) * ((size_t)d + 1) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -216,7 +216,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   a.c = scale * kLog2e;
   a.splits = splits;
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + (size_t)B * H * splits * d;
+  a.part_lse = a.part_o + (size_t)H * B * (splits + 1) * d;
   return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
 }
 
@@ -252,10 +252,12 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   const int Lmax = max_pages_per_seq * page_size;
   const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax) : num_splits;
+  // a work item holds at most ceil(ceil(Lmax / 32) / splits) blocks of 32 keys
   int chunk = (Lmax + splits - 1) / splits;
   chunk = (chunk + 31) / 32 * 32;
   if ((chunk + page_size - 1) / page_size > fattn::kDecodeMaxSplitPages)
-    return fail(FATTN_ERR_UNSUPPORTED, "%s: one split would span %d pages (at most %d); use more splits or larger pages",
+    return fail(FATTN_ERR_UNSUPPORTED,
+                "%s: one work item could span %d pages (at most %d); use more splits or larger pages",
                 fn, (chunk + page_size - 1) / page_size, fattn::kDecodeMaxSplitPages);
   const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
   if (workspace_bytes < need)
@@ -278,7 +280,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   a.c = scale * kLog2e;
   a.splits = splits;
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + (size_t)B * H * splits * d;
+  a.part_lse = a.part_o + (size_t)H * B * (splits + 1) * d;
   a.block_table = block_table;
   a.max_pages = max_pages_per_seq;
   a.page_shift = shift;

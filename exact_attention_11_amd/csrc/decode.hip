@@ -5,21 +5,25 @@
 // bandwidth section).  The design therefore only tries to keep many bytes in
 // flight and to touch each byte once:
 //
-//  * kernel 1, one 64-wide wave per (sequence, kv-head, split): the split owns
-//    a contiguous chunk of cache rows.  The G query heads that share the
-//    kv-head (grouped-query attention) are served by the same pass, so K and V
-//    are streamed once per kv-head.  The G heads are the columns of small
+//  * kernel 1, one 64-wide wave per (kv-head, work item): the cache rows of
+//    all sequences are cut into equal runs of whole 32-key blocks, one per
+//    work item, whatever the lengths (the partition below), so every wave
+//    streams the same bytes and the waves finish together.  A run that crosses
+//    the end of a sequence is processed as one segment per sequence.  The G
+//    query heads that share the kv-head (grouped-query attention) are served
+//    by the same pass, so K and V are streamed once per kv-head.  The G heads are the columns of small
 //    matrix-core products (16x16x32 bf16): scores S^T = K Q^T and output
 //    O^T += V^T P^T, with V^T gathered from LDS by transposing reads.  The
 //    matrix cores are mostly idle doing this, but they take the dot products
 //    off the vector ALUs so that the wave spends its time waiting on HBM, not
 //    computing.  Online softmax per head (base 2, rescaled only when a score
 //    exceeds the reference max by more than 2^8).  The next block's loads are
-//    issued as soon as the current block's registers are consumed.  The
-//    normalised partial output and its natural-log LSE go to the workspace; an
-//    empty chunk writes 0 and -inf.
+//    issued as soon as the current block's registers are consumed.  Each
+//    segment's normalised partial output and its natural-log LSE go to the
+//    workspace.
 //  * kernel 2, one workgroup per (sequence, head): weights exp(lse_c - lse)
-//    with lse = log-sum-exp over the splits, O = sum_c w_c o_c.
+//    with lse = log-sum-exp over the sequence's partials, O = sum_c w_c o_c;
+//    an empty sequence gives O = 0 and LSE = -inf.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -55,44 +59,58 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // land on disjoint banks; bit 0 is never flipped, so 32-byte pieces stay whole.
 __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | (((r >> 2) & 1) << 1); }
 
-// One 64-wide wave per (sequence, kv-head, split).  Blocks of 32 keys:
+// 32-key blocks of sequence b (none past the batch); L = its length clamped
+// to [0, Lmax].
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b, int& L) {
+  L = 0;
+  if (b < a.B) {
+    const int x = a.seqlens[b];
+    L = x < 0 ? 0 : (x > a.Lmax ? a.Lmax : x);
+  }
+  return (L + 31) >> 5;
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Work partition, shared by the split and combine kernels.  Per kv head the
+// 32-key blocks of all sequences are laid end to end: sequence b holds blocks
+// [P_b, P_b + nb_b), nb_b = ceil(L_b / 32), T = sum of nb_b.  With W = B *
+// splits work items and W' = min(W, T), item w takes blocks
+// [floor(w T / W'), floor((w + 1) T / W')): every item streams the same number
+// of cache rows to within one block, whatever the lengths, so the waves finish
+// together.  T >= W' makes every range non-empty, so the items touching
+// sequence b are exactly those from the one holding its first block to the
+// one holding its last; block x lies in item floor(((x + 1) W' - 1) / T).  An
+// item crossing sequence ends writes one partial per sequence; the partial of
+// (sequence b, item w) goes to slot w + b of its head.  In cache order each
+// next segment raises w or b or both, so slots are distinct and below
+// B * (splits + 1).
+__device__ __forceinline__ long long partition_slots(const DecodeArgs& a) { return (long long)a.B * (a.splits + 1); }
+
+// Rows [kb0, kb1) of sequence b, kv head g, by one 64-wide wave.  Blocks of
+// 32 keys:
 //   S^T[32 keys x 16 cols] = K Q^T   (v_mfma_f32_16x16x32_bf16, 2 x 4 steps;
 //                                      column n < G is query head h0 + n, the
 //                                      other columns multiply zeros)
 //   online softmax per column on the accumulator (8 scores per lane)
 //   O^T[128 d x 16 cols] += V^T P^T   (8 steps; V^T from LDS by transposing
 //                                      reads, P^T straight from the scores)
+// The normalised partial and its natural-log LSE go to slot `slot`.
 template <int G, bool PAGED>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chunk) {
+__device__ __forceinline__ void decode_segment(const DecodeArgs& a, unsigned char* sv, int* pt, int g, int b,
+                                               int kb0, int kb1, long long slot) {
   constexpr int NT = G > 16 ? G / 16 : 1;  // 16-column tiles of query heads
-  __shared__ __attribute__((aligned(16))) unsigned char sv[32 * kD * 2];
-  // paged cache: physical page of each logical page this split touches
-  __shared__ int pt[PAGED ? kDecodeMaxSplitPages + 2 : 1];
   const int lane = threadIdx.x;
   const int n16 = lane & 15;  // column (query head) of the 16x16 tiles
   const int g4 = lane >> 4;   // 16-lane group
-
-  const int S = a.splits;
-  int wid = blockIdx.x;
-  const int s = wid % S;
-  wid /= S;
-  const int g = wid % a.Hkv;
-  const int b = wid / a.Hkv;
   const int h0 = g * G;
-
-  int L = a.seqlens[b];
-  L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
-  const int kb0 = s * chunk;
-  const int kb1 = min(L, kb0 + chunk);
-
-  float* po = a.part_o + (((long)b * a.H + h0) * S + s) * kD;  // head hh at + hh*S*kD
-  float* pl = a.part_lse + ((long)b * a.H + h0) * S + s;       // head hh at + hh*S
-
-  if (kb0 >= kb1) {
-    for (int i = lane; i < G * kD; i += 64) po[(long)(i / kD) * S * kD + (i % kD)] = 0.f;
-    if (lane < G) pl[(long)lane * S] = kNegInf;
-    return;
-  }
+  const long long NS = partition_slots(a);
+  float* po = a.part_o + ((long long)h0 * NS + slot) * kD;  // head h0 + hh at + hh*NS*kD
+  float* pl = a.part_lse + (long long)h0 * NS + slot;       // head h0 + hh at + hh*NS
 
   // rows [kb0, kb1) of this kv-head; loads past kb1 read zero
   const long rowbase = ((long)b * a.Hkv + g) * a.Lmax + kb0;
@@ -102,7 +120,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
   const int n = kb1 - kb0;
 
   // paged cache: stage the block-table entries of pages lp0 .. (kb1-1)/P, plus
-  // one (the half block just past the chunk end), clamped to valid pages
+  // one (the half block just past the segment end), clamped to valid pages
   const int sh = a.page_shift;
   const int lp0 = kb0 >> sh;
   if constexpr (PAGED) {
@@ -260,48 +278,121 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, int chun
     const int hh = 16 * t + n16;  // head within the group
     if (hh < G) {
       const float inv = 1.f / lt;
-      float* dst = po + (long)hh * S * kD + 4 * g4;
+      float* dst = po + (long long)hh * NS * kD + 4 * g4;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
         stg16(dst + 16 * db, u32x4{__float_as_uint(acc[t][db][0] * inv), __float_as_uint(acc[t][db][1] * inv),
                                    __float_as_uint(acc[t][db][2] * inv), __float_as_uint(acc[t][db][3] * inv)});
-      if (g4 == 0) pl[(long)hh * S] = (m[t] + log2_hw(lt)) * kLn2;
+      if (g4 == 0) pl[(long long)hh * NS] = (m[t] + log2_hw(lt)) * kLn2;
     }
   }
 }
 
-// One workgroup per (sequence, head); wave w sums splits w, w+4, ...; every
-// lane owns 2 d values.
+// One 64-wide wave per (kv head, work item): walks the segments of its block
+// range in cache order.
+template <int G, bool PAGED>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char sv[32 * kD * 2];
+  // paged cache: physical page of each logical page one segment touches
+  __shared__ int pt[PAGED ? kDecodeMaxSplitPages + 2 : 1];
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x % a.Hkv;
+  const long long w = blockIdx.x / a.Hkv;
+
+  long long T = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    int L;
+    T += wave_sum_ll(seq_blocks(a, base + lane, L));
+  }
+  const long long W = (long long)a.B * a.splits;
+  const long long Wp = W < T ? W : T;
+  if (w >= Wp) return;  // also every wave when all sequences are empty
+  const long long lo = w * T / Wp, hi = (w + 1) * T / Wp;
+
+  long long carry = 0;  // blocks of the sequences before this group of 64
+  for (int base = 0; base < a.B && carry < hi; base += 64) {
+    int L;
+    const int nb = seq_blocks(a, base + lane, L);
+    long long x = nb;  // inclusive prefix sum over the group
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    const long long P = carry + x - nb;
+    unsigned long long act = __ballot((P > lo ? P : lo) < (P + nb < hi ? P + nb : hi));
+    while (act) {
+      const int i = __builtin_ctzll(act);
+      act &= act - 1;
+      const long long Pb = __shfl(P, i, 64);
+      const int Lb = __builtin_amdgcn_readfirstlane(__shfl(L, i, 64));
+      const long long s0 = Pb > lo ? Pb : lo;
+      const long long e = Pb + ((Lb + 31) >> 5);
+      const long long s1 = e < hi ? e : hi;
+      const int kb0 = __builtin_amdgcn_readfirstlane((int)((s0 - Pb) * 32));
+      const int kb1 = __builtin_amdgcn_readfirstlane(min(Lb, (int)((s1 - Pb) * 32)));
+      decode_segment<G, PAGED>(a, sv, pt, g, base + i, kb0, kb1, w + base + i);
+    }
+    carry += __shfl(x, 63, 64);
+  }
+}
+
+// One workgroup per (sequence, head).  The partials of sequence b are the
+// slots of the work items that touch it (see the partition above), found from
+// the same prefix sums; wave w sums slots w, w+4, ...; every lane owns 2 d
+// values.
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float part[kCombineWaves][kD];
   const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int S = a.splits;
-  const float* pl = a.part_lse + (long)bh * S;
-  const float* po = a.part_o + (long)bh * S * kD;
 
-  const float lse_s = lane < S ? pl[lane] : kNegInf;
-  const float M = wave_max(lse_s);
+  long long T = 0, P = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    int L;
+    const int nb = seq_blocks(a, base + lane, L);
+    T += wave_sum_ll(nb);
+    P += wave_sum_ll(base + lane < b ? nb : 0);
+  }
+  int Lb;
+  const int nbb = seq_blocks(a, b, Lb);
   uint16_t* o = (uint16_t*)a.o + (long)bh * kD;
-  if (M == kNegInf) {  // uniform over the workgroup
+  if (nbb == 0) {  // empty sequence (uniform over the workgroup)
     if (tid < kD / 2) reinterpret_cast<uint32_t*>(o)[tid] = 0u;
     if (a.lse != nullptr && tid == 0) a.lse[bh] = kNegInf;
     return;
   }
-  const float w = lane < S ? exp2_hw((lse_s - M) * kLog2e) : 0.f;
-  const float W = wave_sum(w);
+  const long long W = (long long)a.B * a.splits;
+  const long long Wp = W < T ? W : T;
+  const long long wf = ((P + 1) * Wp - 1) / T;    // item holding the first block
+  const long long wl = ((P + nbb) * Wp - 1) / T;  // item holding the last block
+  const int n = (int)(wl - wf + 1);
+  const long long NS = partition_slots(a);
+  const float* pl = a.part_lse + (long long)h * NS + wf + b;
+  const float* po = a.part_o + ((long long)h * NS + wf + b) * kD;
+
+  float M = kNegInf;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, pl[i]);
+  M = wave_max(M);
+  float Wsum = 0.f;
+  for (int i = lane; i < n; i += 64) Wsum += exp2_hw((pl[i] - M) * kLog2e);
+  Wsum = wave_sum(Wsum);
+
   float acc0 = 0.f, acc1 = 0.f;
-  // at most 64 splits: 16 per wave, all loads independent
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const float w = i0 + lane < n ? exp2_hw((pl[i0 + lane] - M) * kLog2e) : 0.f;
+    // 16 slots per wave, all loads independent
 #pragma unroll
-  for (int i = 0; i < 64 / kCombineWaves; ++i) {
-    const int s = wv + kCombineWaves * i;
-    const float ws = __shfl(w, s & 63, 64);
-    if (s < S) {
-      const float2 v = *reinterpret_cast<const float2*>(po + (long)s * kD + 2 * lane);
-      acc0 = __builtin_fmaf(ws, v.x, acc0);
-      acc1 = __builtin_fmaf(ws, v.y, acc1);
+    for (int k = 0; k < 64 / kCombineWaves; ++k) {
+      const int s = wv + kCombineWaves * k;
+      const float ws = __shfl(w, s, 64);
+      if (i0 + s < n) {
+        const float2 v = *reinterpret_cast<const float2*>(po + (long)(i0 + s) * kD + 2 * lane);
+        acc0 = __builtin_fmaf(ws, v.x, acc0);
+        acc1 = __builtin_fmaf(ws, v.y, acc1);
+      }
     }
   }
   part[wv][2 * lane] = acc0;
@@ -314,19 +405,19 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
       r0 += part[x][2 * tid];
       r1 += part[x][2 * tid + 1];
     }
-    const float inv = 1.f / W;
+    const float inv = 1.f / Wsum;
     reinterpret_cast<uint32_t*>(o)[tid] = pack_bf16x2(r0 * inv, r1 * inv);
   }
-  if (a.lse != nullptr && tid == 0) a.lse[bh] = M + log2_hw(W) * kLn2;
+  if (a.lse != nullptr && tid == 0) a.lse[bh] = M + log2_hw(Wsum) * kLn2;
 }
 
 template <int G>
-hipError_t launch_g(const DecodeArgs& a, int chunk, hipStream_t stream) {
-  const long grid = (long)a.B * a.Hkv * a.splits;
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  const long grid = (long)a.Hkv * a.B * a.splits;
   if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
+    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3((unsigned)grid), dim3(64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3((unsigned)grid), dim3(64), 0, stream, a, chunk);
+    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3((unsigned)grid), dim3(64), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -338,10 +429,11 @@ hipError_t launch_g(const DecodeArgs& a, int chunk, hipStream_t stream) {
 }  // namespace
 
 int decode_auto_splits(int B, int Hkv, int Lmax) {
-  // One work item per resident wave: 256 CUs x 4 SIMDs x 2 waves.  Work items
-  // that all start together and stream equal chunks finish together, so HBM
-  // stays saturated to the end; more items than slots leave a half-empty
-  // second round.  Chunks stay at least 256 keys; at most 64 splits.
+  // About one work item per resident wave: 256 CUs x 4 SIMDs x 2 waves, the
+  // B * Hkv * splits items all start together and, streaming equal runs, finish
+  // together, so HBM stays saturated to the end; more items than slots leave a
+  // half-empty second round.  The work items a sequence of Lmax keys would
+  // get hold at least 256 keys each; at most 64 splits.
   const long pairs = (long)B * Hkv;
   long s = pairs > 0 ? 2048 / pairs : 64;
   const long smax = (Lmax + 255) / 256;
@@ -354,15 +446,13 @@ int decode_auto_splits(int B, int Hkv, int Lmax) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.d != kD) return hipErrorInvalidValue;
   if (a.B == 0) return hipSuccess;
-  int chunk = (a.Lmax + a.splits - 1) / a.splits;
-  chunk = (chunk + 31) / 32 * 32;  // whole 32-key blocks
   switch (a.H / a.Hkv) {
-    case 1: return launch_g<1>(a, chunk, stream);
-    case 2: return launch_g<2>(a, chunk, stream);
-    case 4: return launch_g<4>(a, chunk, stream);
-    case 8: return launch_g<8>(a, chunk, stream);
-    case 16: return launch_g<16>(a, chunk, stream);
-    case 32: return launch_g<32>(a, chunk, stream);
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    case 16: return launch_g<16>(a, stream);
+    case 32: return launch_g<32>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,9 +54,9 @@ struct DecodeArgs {
   float* lse;
   int B, H, Hkv, Lmax, d;
   float c;  // scale * log2(e)
-  int splits;
-  float* part_o;    // [B, H, splits, d]
-  float* part_lse;  // [B, H, splits]
+  int splits;       // work items per kv head: B * splits
+  float* part_o;    // [H, B * (splits + 1), d]: partial of (sequence b, item w) at slot w + b
+  float* part_lse;  // [H, B * (splits + 1)]
   // paged cache (block_table != null): k, v are [num_pages, Hkv, 2^page_shift, d]
   // and sequence b's logical page p is physical page block_table[b*max_pages + p]
   const int32_t* block_table;
@@ -65,8 +65,8 @@ struct DecodeArgs {
   int num_pages;
 };
 
-// Most page-table entries one decode split stages in LDS (a split covers at
-// most this many pages plus one).
+// Most page-table entries one decode segment stages in LDS (a segment covers
+// at most this many pages plus one).
 constexpr int kDecodeMaxSplitPages = 2047;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -92,7 +92,8 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
 /*
  * attn_decode_workspace_bytes -- device workspace attn_decode needs for this
  * shape: room for one partial output row (f32, d values) and one partial
- * log-sum-exp (f32) per (b, h, split), rounded up to 256 bytes.
+ * log-sum-exp (f32) per (head, slot), B * (num_splits + 1) slots per head,
+ * rounded up to 256 bytes.
  * num_splits == 0 asks for the automatic choice attn_decode would make for
  * the given Lmax (pass it as lmax_hint; ignored otherwise).  Returns 0 for an
  * invalid shape.
@@ -106,8 +107,10 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  * Decode is the bandwidth-bound step the ledger page describes (bandwidth
  * section: s_j = q^T k_j over all history keys, o = sum_j p_j v_j, O(n d)
  * bytes per step), and prefill and decode take different kernels (CANN
- * ops-transformer FlashAttention page, prefill vs decode).  Kernel 1 gives
- * each (sequence, kv-head, split) a contiguous chunk of keys and writes a
+ * ops-transformer FlashAttention page, prefill vs decode).  Kernel 1 lays the
+ * 32-key blocks of all sequences end to end and gives each (kv-head, work
+ * item) an equal run of them, B * num_splits items per kv head, so the work is
+ * even whatever the lengths; for each sequence its run touches it writes a
  * normalised partial output and its log-sum-exp to the workspace; kernel 2
  * combines the partials of each (sequence, head).
  *
@@ -122,10 +125,10 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  *   lse        f32  [B, H]               written, or NULL
  *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16, 32} (32: multi-query
  *              attention with 32 heads); d == 128; scale finite, >= 0.
- *   num_splits 0 = automatic (about one work item per resident wave), else 1..64: the
- *              key range [0, Lmax) is cut into num_splits equal chunks
- *              (rounded up to whole 32-key blocks); split s of sequence b
- *              covers the part of chunk s below seqlens_k[b].
+ *   num_splits 0 = automatic (about one work item per resident wave), else
+ *              1..64: work items per sequence on average.  The T blocks
+ *              (ceil(seqlens_k[b] / 32) per sequence, summed) are cut into
+ *              min(B * num_splits, T) runs of floor/ceil(T / items) blocks.
  *   workspace  device buffer of at least attn_decode_workspace_bytes(...)
  *              bytes for the same arguments; contents on entry are ignored.
  */

@@ -118,13 +118,14 @@ def test_attn_decode_rejects(kw, status):
 
 
 def test_decode_workspace_size():
-    # one f32 row of d plus one f32 LSE per (b, h, split), rounded to 256 B
-    assert fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 64) == 16 * 32 * 64 * 129 * 4
-    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 1) == 768
-    # automatic split count for Lmax = 1 is one split: 4128 bytes -> 4352
-    assert fa.attn_decode_workspace_bytes(2, 4, 2, 1, 128, 0) == 4352
+    # one f32 row of d plus one f32 LSE per (head, slot), B * (splits + 1)
+    # slots per head, rounded to 256 B
+    assert fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 64) == 32 * 16 * 65 * 129 * 4
+    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 1) == 1280  # 1032 -> 1280
+    # automatic split count for Lmax = 1 is one split: 8256 bytes -> 8448
+    assert fa.attn_decode_workspace_bytes(2, 4, 2, 1, 128, 0) == 8448
     auto = fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 0)
-    assert auto == 16 * 32 * 16 * 129 * 4  # 16 x 8 (sequence, kv-head) pairs -> 16 splits
+    assert auto == 32 * 16 * 17 * 129 * 4  # 16 x 8 (sequence, kv-head) pairs -> 16 splits
     assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 65) == 0
     assert fa.attn_decode_workspace_bytes(1, 0, 1, 10, 128, 1) == 0
 

@@ -457,6 +457,41 @@ def test_decode_clamps_lengths_to_the_cache():
     assert_lse(lse[[0, 3]], L_ref)
 
 
+@pytest.mark.parametrize("splits", [1, 16])
+def test_decode_partition_many_short_sequences(splits):
+    """The work partition over sequence ends: 70 sequences (two groups of 64 in
+    the kernels' prefix sums) of 0..96 keys.  With 1 split the 70 work items
+    hold one or two blocks each and most cross a sequence end; with 16 there
+    are more items than blocks, so only one item per block runs."""
+    _need_gpu()
+    B = 70
+    c = W.Decode("decode_short", B, 8, 2, 96, 128, 1 / math.sqrt(128), 1, 96, 35)
+    x = W.decode_inputs(c, seqlens=[(7 * b) % 97 for b in range(B)])
+    o, lse = run_decode(x, splits)
+    empty = x.seqlens == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    keep = np.flatnonzero(~empty)
+    O_ref, L_ref = decode_ref(x, keep)
+    assert_bf16(o[keep], O_ref, f"splits={splits}")
+    assert_lse(lse[keep], L_ref, f"splits={splits}")
+
+
+def test_decode_partition_one_long_sequence():
+    """One sequence holds nearly all the blocks, so it is spread over ~126 of
+    the 128 work items and the combine merges more than 64 partials; the other
+    sequences are empty or a single block."""
+    _need_gpu()
+    c = W.Decode("decode_skew", 8, 16, 2, 9000, 128, 1 / math.sqrt(128), 1, 9000, 36)
+    x = W.decode_inputs(c, seqlens=[9000, 0, 5, 0, 0, 32, 0, 1])
+    o, lse = run_decode(x, 16)
+    empty = x.seqlens == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    keep = np.flatnonzero(~empty)
+    O_ref, L_ref = decode_ref(x, keep)
+    assert_bf16(o[keep], O_ref)
+    assert_lse(lse[keep], L_ref)
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_hstu_rows_past_max_seqlen_are_not_computed(causal):
     """A sequence longer than max_seqlen (a violated precondition) is cut to
