@@ -306,7 +306,7 @@ def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, 
     wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, 64)
     ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
     sweep = {}
-    for sp in (16, 32, 64):
+    for sp in (4, 8, 16, 32):
         ms_d = _time_calls(lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
                                                   dc.scale, sp, ws, wsb), stream, reps=20)
         sweep[str(sp)] = {"GB/s": round(nbytes / (ms_d * 1e-3) / 1e9, 1), "ms_per_call": round(ms_d, 4)}

@@ -167,7 +167,10 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
   int s = num_splits;
   if (s == 0) {
     if (lmax_hint < 1) return 0;
-    s = fattn::decode_auto_splits(B, Hkv, lmax_hint);
+    // large enough for either cache layout's automatic count
+    const int sc = fattn::decode_auto_splits(B, Hkv, lmax_hint, false);
+    const int sp = fattn::decode_auto_splits(B, Hkv, lmax_hint, true);
+    s = sc > sp ? sc : sp;
   }
   const size_t bytes = (size_t)H * B * (s + 1) * ((size_t)d + 1) * sizeof(float);
   return (bytes + 255) / 256 * 256;
@@ -196,7 +199,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
       (lse && !aligned16(lse)))
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if ((double)B * Hkv * Lmax * d > 9.0e15) return fail(FATTN_ERR_INVALID_ARG, "%s: cache too large", fn);
-  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax) : num_splits;
+  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax, false) : num_splits;
   const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
   if (workspace_bytes < need)
     return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
@@ -251,7 +254,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
       (lse && !aligned16(lse)))
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   const int Lmax = max_pages_per_seq * page_size;
-  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax) : num_splits;
+  const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax, true) : num_splits;
   // a work item holds at most ceil(ceil(Lmax / 32) / splits) blocks of 32 keys
   int chunk = (Lmax + splits - 1) / splits;
   chunk = (chunk + 31) / 32 * 32;

@@ -428,16 +428,25 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int decode_auto_splits(int B, int Hkv, int Lmax) {
-  // About one work item per resident wave: 256 CUs x 4 SIMDs x 2 waves, the
-  // B * Hkv * splits items all start together and, streaming equal runs, finish
-  // together, so HBM stays saturated to the end; more items than slots leave a
-  // half-empty second round.  The work items a sequence of Lmax keys would
-  // get hold at least 256 keys each; at most 64 splits.
+int decode_auto_splits(int B, int Hkv, int Lmax, bool paged) {
+  // About 768 work items (three per CU) for a contiguous cache and 1024 for
+  // a paged one, whose extra page-table step per block wants more waves in
+  // flight.  The B * Hkv * splits items start together and, streaming equal
+  // runs, finish together.  Measured on the GQA decode workload
+  // (B * Hkv = 128), contiguous: 768 items 6.68 TB/s, 512 6.56, 1024 6.59,
+  // 1536 6.54, 2048 6.37; paged (16-key pages): 768 6.00, 1024 6.40, 1536
+  // 6.10, 2048 6.19.  Counts that leave the CUs unevenly loaded are slower
+  // (contiguous, 896: 6.10, 2560: 5.86).  The work items a sequence of Lmax
+  // keys would get hold at least 256 keys each, and at most the keys of
+  // kDecodeMaxSplitPages pages of the smallest size (16 keys); at most 64
+  // splits.
   const long pairs = (long)B * Hkv;
-  long s = pairs > 0 ? 2048 / pairs : 64;
+  long s = pairs > 0 ? (paged ? 1024 : 768) / pairs : 64;
   const long smax = (Lmax + 255) / 256;
   if (s > smax) s = smax;
+  const long item_max = (long)kDecodeMaxSplitPages * 16 / 32 * 32;  // whole 32-key blocks
+  const long smin = (Lmax + item_max - 1) / item_max;
+  if (s < smin) s = smin;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;

@@ -71,8 +71,8 @@ constexpr int kDecodeMaxSplitPages = 2047;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
-// Automatic split count for a decode shape.
-int decode_auto_splits(int B, int Hkv, int Lmax);
+// Automatic split count for a decode shape (contiguous or paged cache).
+int decode_auto_splits(int B, int Hkv, int Lmax, bool paged);
 
 struct Fp8Args {
   const void* q;            // [B, H, N, d] E4M3

@@ -94,9 +94,10 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
  * shape: room for one partial output row (f32, d values) and one partial
  * log-sum-exp (f32) per (head, slot), B * (num_splits + 1) slots per head,
  * rounded up to 256 bytes.
- * num_splits == 0 asks for the automatic choice attn_decode would make for
- * the given Lmax (pass it as lmax_hint; ignored otherwise).  Returns 0 for an
- * invalid shape.
+ * num_splits == 0 asks for room for the automatic choice, the larger of the
+ * counts attn_decode and attn_decode_paged would make for the given Lmax
+ * (pass it as lmax_hint; ignored otherwise), so one buffer serves both.
+ * Returns 0 for an invalid shape.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits);
 
@@ -125,7 +126,8 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  *   lse        f32  [B, H]               written, or NULL
  *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16, 32} (32: multi-query
  *              attention with 32 heads); d == 128; scale finite, >= 0.
- *   num_splits 0 = automatic (about one work item per resident wave), else
+ *   num_splits 0 = automatic (about 768 work items in all, 1024 for the
+ *              paged cache; raised for very long caches), else
  *              1..64: work items per sequence on average.  The T blocks
  *              (ceil(seqlens_k[b] / 32) per sequence, summed) are cut into
  *              min(B * num_splits, T) runs of floor/ceil(T / items) blocks.

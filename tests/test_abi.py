@@ -125,7 +125,11 @@ def test_decode_workspace_size():
     # automatic split count for Lmax = 1 is one split: 8256 bytes -> 8448
     assert fa.attn_decode_workspace_bytes(2, 4, 2, 1, 128, 0) == 8448
     auto = fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 0)
-    assert auto == 32 * 16 * 17 * 129 * 4  # 16 x 8 (sequence, kv-head) pairs -> 16 splits
+    # 16 x 8 (sequence, kv-head) pairs: 6 splits (768 items) contiguous, 8 (1024) paged; room for 8
+    assert auto == 32 * 16 * 9 * 129 * 4
+    # a long cache raises the automatic count so that no work item spans more
+    # than 2047 pages of 16 keys: Lmax = 10^6 -> ceil(10^6 / 32736) = 31 splits
+    assert fa.attn_decode_workspace_bytes(16, 32, 8, 1_000_000, 128, 0) == 32 * 16 * 32 * 129 * 4
     assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 65) == 0
     assert fa.attn_decode_workspace_bytes(1, 0, 1, 10, 128, 1) == 0
 

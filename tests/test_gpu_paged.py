@@ -129,3 +129,33 @@ def test_paged_clamps_table_entries_and_lengths():
     o, lse = run_paged(bad, 0)
     assert_bf16(bf16_dev_to_f64(o), O_ref, "clamped table and lengths")
     assert_lse(lse.cpu().numpy(), L_ref, "clamped table and lengths")
+
+
+def test_paged_auto_splits_with_a_long_page_table():
+    """Automatic split count with 128 (sequence, kv-head) pairs and a table of
+    12,800 pages of 16 keys (Lmax = 204,800): the count is raised until no
+    work item can span more than 2047 pages, so the call is accepted, and the
+    short sequences still match the oracle.  Table entries past each
+    sequence's pages are 0 and never read for keys."""
+    _need_gpu()
+    B, P, wide = 128, 16, 12800
+    c = W.Decode("paged_wide_table", B, 1, 1, 96, 128, 1 / math.sqrt(128), 1, 96, 55)
+    x = W.decode_inputs(c, seqlens=[(5 * b) % 97 for b in range(B)])
+    px = W.paged_from_decode(x, P, perm_seed=55)
+    table = np.zeros((B, wide), dtype=np.int32)
+    table[:, :px.block_table.shape[1]] = px.block_table
+    q, kp, vp = to_dev_bf16(x.q), to_dev_bf16(px.k_pages), to_dev_bf16(px.v_pages)
+    o = torch.empty((B, 1, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1), dtype=torch.float32, device="cuda")
+    nbytes = fa.attn_decode_workspace_bytes(B, 1, 1, wide * P, 128, 0)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    fa.attn_decode_paged(q, kp, vp, to_dev(table), to_dev(x.seqlens), o, lse, B, 1, 1, P, wide, px.num_pages, 128,
+                         c.scale, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    O_ref, L_ref = paged_ref(px)
+    o64, l64 = bf16_dev_to_f64(o), lse.cpu().numpy()
+    empty = x.seqlens == 0
+    assert np.all(o64[empty] == 0) and np.all(np.isneginf(l64[empty]))
+    keep = np.flatnonzero(~empty)
+    assert_bf16(o64[keep], O_ref[keep])
+    assert_lse(l64[keep], L_ref[keep])
