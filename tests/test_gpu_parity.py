@@ -304,6 +304,17 @@ def test_decode_zero_length_sequence():
     assert_lse(lse[1:], L_ref)
 
 
+@pytest.mark.parametrize("splits", [0, 5])
+def test_decode_every_sequence_empty(splits):
+    """No key blocks at all: every work item exits at once and the combine
+    alone writes O = 0 and LSE = -inf for every (sequence, head)."""
+    _need_gpu()
+    c = W.Decode("decode_all_empty", 3, 8, 2, 64, 128, 0.1, 1, 64, 37)
+    x = W.decode_inputs(c, seqlens=[0, 0, 0])
+    o, lse = run_decode(x, splits)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
 def test_decode_reused_workspace_with_random_contents():
     """The workspace needs no clearing: random bytes on entry, then calls with
     other split counts on the same buffer, each checked against the oracle;
