@@ -373,25 +373,46 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
   const float* pl = a.part_lse + (long long)h * NS + wf + b;
   const float* po = a.part_o + ((long long)h * NS + wf + b) * kD;
 
-  float M = kNegInf;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, pl[i]);
-  M = wave_max(M);
-  float Wsum = 0.f;
-  for (int i = lane; i < n; i += 64) Wsum += exp2_hw((pl[i] - M) * kLog2e);
-  Wsum = wave_sum(Wsum);
-
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const float w = i0 + lane < n ? exp2_hw((pl[i0 + lane] - M) * kLog2e) : 0.f;
-    // 16 slots per wave, all loads independent
+  float M, Wsum, acc0 = 0.f, acc1 = 0.f;
+  constexpr int kPerWave = 64 / kCombineWaves;
+  if (n <= 64) {
+    // one load of every LSE and every partial row this wave sums, all issued
+    // before the reductions that weight them
+    const float ls = lane < n ? pl[lane] : kNegInf;
+    float2 v[kPerWave];
 #pragma unroll
-    for (int k = 0; k < 64 / kCombineWaves; ++k) {
+    for (int k = 0; k < kPerWave; ++k) {
       const int s = wv + kCombineWaves * k;
-      const float ws = __shfl(w, s, 64);
-      if (i0 + s < n) {
-        const float2 v = *reinterpret_cast<const float2*>(po + (long)(i0 + s) * kD + 2 * lane);
-        acc0 = __builtin_fmaf(ws, v.x, acc0);
-        acc1 = __builtin_fmaf(ws, v.y, acc1);
+      v[k] = s < n ? *reinterpret_cast<const float2*>(po + (long)s * kD + 2 * lane) : make_float2(0.f, 0.f);
+    }
+    M = wave_max(ls);
+    const float w = lane < n ? exp2_hw((ls - M) * kLog2e) : 0.f;
+    Wsum = wave_sum(w);
+#pragma unroll
+    for (int k = 0; k < kPerWave; ++k) {
+      const float ws = __shfl(w, wv + kCombineWaves * k, 64);
+      acc0 = __builtin_fmaf(ws, v[k].x, acc0);
+      acc1 = __builtin_fmaf(ws, v[k].y, acc1);
+    }
+  } else {
+    M = kNegInf;
+    for (int i = lane; i < n; i += 64) M = fmaxf(M, pl[i]);
+    M = wave_max(M);
+    Wsum = 0.f;
+    for (int i = lane; i < n; i += 64) Wsum += exp2_hw((pl[i] - M) * kLog2e);
+    Wsum = wave_sum(Wsum);
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const float w = i0 + lane < n ? exp2_hw((pl[i0 + lane] - M) * kLog2e) : 0.f;
+      // 16 slots per wave, all loads independent
+#pragma unroll
+      for (int k = 0; k < kPerWave; ++k) {
+        const int s = wv + kCombineWaves * k;
+        const float ws = __shfl(w, s, 64);
+        if (i0 + s < n) {
+          const float2 v = *reinterpret_cast<const float2*>(po + (long)(i0 + s) * kD + 2 * lane);
+          acc0 = __builtin_fmaf(ws, v.x, acc0);
+          acc1 = __builtin_fmaf(ws, v.y, acc1);
+        }
       }
     }
   }
