@@ -159,3 +159,26 @@ def test_paged_auto_splits_with_a_long_page_table():
     keep = np.flatnonzero(~empty)
     assert_bf16(o64[keep], O_ref[keep])
     assert_lse(l64[keep], L_ref[keep])
+
+
+@pytest.mark.parametrize("P", [16, 64])
+@pytest.mark.parametrize("splits", [1, 16])
+def test_paged_partition_many_short_sequences(P, splits):
+    """The work partition over sequence ends on the paged cache: 70 sequences
+    of 0..96 keys (two groups of 64 in the prefix sums), so work items start
+    and end inside pages and cross many sequence ends (1 split), or hold one
+    block each (16 splits)."""
+    _need_gpu()
+    B = 70
+    c = W.Decode("paged_short", B, 8, 2, 96, 128, 1 / math.sqrt(128), 1, 96, 56)
+    x = W.decode_inputs(c, seqlens=[(7 * b) % 97 for b in range(B)])
+    px = W.paged_from_decode(x, P, perm_seed=P + splits)
+    o, lse = run_paged(px, splits)
+    O_ref, L_ref = paged_ref(px)
+    o64, l64 = bf16_dev_to_f64(o), lse.cpu().numpy()
+    tag = f"P={P} splits={splits}"
+    empty = x.seqlens == 0
+    assert np.all(o64[empty] == 0) and np.all(np.isneginf(l64[empty])), tag
+    keep = np.flatnonzero(~empty)
+    assert_bf16(o64[keep], O_ref[keep], tag)
+    assert_lse(l64[keep], L_ref[keep], tag)
