@@ -212,37 +212,58 @@ def read_traffic():
 
 
 def cpu_baseline(x, case, seconds: float):
-    """The fp64 oracle as it stands, on a bounded sample of the prefill
-    workload: whole (b, h) heads, all rows, until about `seconds` elapsed."""
+    """The C++ fp64 oracle as it stands (S and P materialised per row panel,
+    two-pass softmax, plain loops, OpenMP over (batch, head, panel)) on a
+    bounded sample of the prefill workload: whole (b, h) heads, all rows, one
+    head per host thread per call, until about `seconds` of compute; then the
+    d=64 causal prefill (B=1, H=32, N=4096) on one thread for about a quarter
+    of that.  Converting the bf16 inputs to fp64 is not timed."""
+    import numpy as np
+
     import oracle
+    from oracle import cpp as ocpp
+    from synthgen import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
-    done = 0
-    t0 = time.perf_counter()
-    for (b, h) in heads:
-        g = h // (case.H // case.Hkv)
-        q = x.f64("q", (slice(b, b + 1), slice(h, h + 1)))
-        k = x.f64("k", (slice(b, b + 1), slice(g, g + 1)))
-        v = x.f64("v", (slice(b, b + 1), slice(g, g + 1)))
-        oracle.attention_forward(q, k, v, case.scale, case.causal)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
+    threads = ocpp.max_threads()
     per_head = 2 * case.N * case.N * case.d * (1 if case.causal else 2)
+    group = case.H // case.Hkv
+    done, el = 0, 0.0
+    while done < case.B * case.H and el < seconds:
+        b, h0 = divmod(done, case.H)
+        h1 = min(case.H, h0 + threads)
+        q = x.f64("q", (slice(b, b + 1), slice(h0, h1)))
+        kv_heads = [h // group for h in range(h0, h1)]  # one kv head per query head, in order
+        k = x.f64("k", (slice(b, b + 1), kv_heads))
+        v = x.f64("v", (slice(b, b + 1), kv_heads))
+        ts = time.perf_counter()
+        oracle.attention_forward(q, k, v, case.scale, case.causal)
+        el += time.perf_counter() - ts
+        done += h1 - h0
+    c1 = W.PREFILL_D64
+    x1 = W.dense_inputs(c1)
+    per_head1 = 2 * c1.N * c1.N * c1.d
+    done1, el1 = 0, 0.0
+    ocpp.set_threads(1)
+    try:
+        while done1 < c1.H and el1 < seconds / 4:
+            q, k, v = (np.ascontiguousarray(x1.f64(n, (slice(0, 1), slice(done1, done1 + 1)))) for n in "qkv")
+            ts = time.perf_counter()
+            oracle.attention_forward(q, k, v, c1.scale, True)
+            el1 += time.perf_counter() - ts
+            done1 += 1
+    finally:
+        ocpp.set_threads(threads)
     return {
         "value": round(done * per_head / el / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} (b,h) heads of the B={case.B} H={case.H} N={case.N} d={case.d} "
-                  f"{'causal' if case.causal else 'non-causal'} prefill, all rows, fp64 numpy, {el:.1f} s",
+        "sample": f"{done} of {case.B * case.H} (b,h) heads of the B={case.B} H={case.H} N={case.N} d={case.d} "
+                  f"{'causal' if case.causal else 'non-causal'} prefill, all rows, C++ fp64 oracle on {threads} "
+                  f"threads, {el:.1f} s of compute",
+        "one_core": {"value": round(done1 * per_head1 / el1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                     "sample": f"{done1} of {c1.H} heads of the B=1 H=32 N=4096 d=64 causal prefill, C++ fp64 "
+                               f"oracle on 1 thread, {el1:.1f} s of compute"},
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
     }
