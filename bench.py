@@ -48,11 +48,40 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (twice the bf16 rate)
+SIMDS = 1024                # 256 CUs x 4 SIMDs
+SPEC_CLOCK_HZ = 2.4e9
+# Issue cycles of one 64-lane transcendental instruction (v_exp_f32) on one
+# SIMD, measured with an in-bounds microbenchmark (v_rcp_f32 taken at the
+# same rate): the HSTU weight needs two per score.
+TRANS_CYCLES_PER_WAVE_OP = 8.5
 TILE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/tile_bf16.hip", "exact_attention_11_amd/csrc/common.hpp",
                        "exact_attention_11_amd/csrc/launch.hpp"]
 DECODE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/decode.hip", "exact_attention_11_amd/csrc/common.hpp",
                          "exact_attention_11_amd/csrc/launch.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tile_bf16_prefill_d128_causal_traffic.txt")
+
+
+def prefill_flops(B, H, N, d, causal) -> int:
+    """Ledger page convention: two products of 2 n^2 d per (b, h), causal
+    counted as half (HSTU page, optimisation two)."""
+    return B * H * 4 * N * N * d // (2 if causal else 1)
+
+
+def backward_flops(B, H, N, d, causal) -> int:
+    """Five products of 2 n^2 d per (b, h) (S, dP, dV, dQ, dK), causal halved."""
+    return B * H * 10 * N * N * d // (2 if causal else 1)
+
+
+def hstu_flops(lengths, H, d, causal=True) -> int:
+    """The prefill convention summed over the jagged sequences."""
+    return H * sum(4 * int(L) * int(L) * d for L in lengths) // (2 if causal else 1)
+
+
+def decode_bytes(seqlens, B, H, Hkv, d) -> int:
+    """Algorithmic bytes of one decode call: K and V rows [0, L_b) once per kv
+    head, q and O once, LSE and the lengths once (the workspace partials are
+    overhead, not algorithmic)."""
+    return int(sum(int(L) for L in seqlens)) * Hkv * d * 2 * 2 + 2 * B * H * d * 2 + B * H * 4 + B * 4
 
 
 def sources_sha(paths) -> str:
@@ -225,7 +254,7 @@ def cpu_baseline(x, case, seconds: float):
     from synthgen import workloads as W
 
     threads = ocpp.max_threads()
-    per_head = 2 * case.N * case.N * case.d * (1 if case.causal else 2)
+    per_head = prefill_flops(1, 1, case.N, case.d, case.causal)
     group = case.H // case.Hkv
     done, el = 0, 0.0
     while done < case.B * case.H and el < seconds:
@@ -241,7 +270,7 @@ def cpu_baseline(x, case, seconds: float):
         done += h1 - h0
     c1 = W.PREFILL_D64
     x1 = W.dense_inputs(c1)
-    per_head1 = 2 * c1.N * c1.N * c1.d
+    per_head1 = prefill_flops(1, 1, c1.N, c1.d, True)
     done1, el1 = 0, 0.0
     ocpp.set_threads(1)
     try:
@@ -304,7 +333,7 @@ def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, 
 
     ctx = {}
     # the headline shape without the causal mask: 4 n^2 d per (b, h)
-    f = 4 * pc.N * pc.N * pc.d * pc.B * pc.H
+    f = prefill_flops(pc.B, pc.H, pc.N, pc.d, False)
     ms_nc = _time_calls(lambda: fa.attn_fwd(q, k, v, o, lse, pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 0), stream)
     ctx["prefill_noncausal"] = {"workload": "B=8 H=32 N=4096 d=128 bf16 non-causal", "ms_per_call": round(ms_nc, 4),
                                 "TFLOP/s": round(f / (ms_nc * 1e-3) / 1e12, 2),
@@ -317,17 +346,17 @@ def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, 
         co = torch.empty_like(cq)
         cl = torch.empty((c.B, c.H, c.N), dtype=torch.float32, device=dev)
         ms_c = _time_calls(lambda: fa.attn_fwd(cq, ck, cv, co, cl, c.B, c.H, c.Hkv, c.N, c.d, c.scale, 1), stream)
-        fc = 2 * c.N * c.N * c.d * c.B * c.H
+        fc = prefill_flops(c.B, c.H, c.N, c.d, True)
         ctx[key] = {"workload": label, "ms_per_call": round(ms_c, 4), "TFLOP/s": round(fc / (ms_c * 1e-3) / 1e12, 2),
                     "frac_bf16_peak": round(fc / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del cq, ck, cv, co, cl
     # decode at fixed split counts (the timed step uses the automatic count)
     ssum = int(dx.seqlens.sum())
-    nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
-    wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, 64)
+    nbytes = decode_bytes(dx.seqlens, dc.B, dc.H, dc.Hkv, dc.d)
+    wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, 8)
     ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
     sweep = {}
-    for sp in (4, 8, 16, 32):
+    for sp in (4, 8):
         ms_d = _time_calls(lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
                                                   dc.scale, sp, ws, wsb), stream, reps=20)
         sweep[str(sp)] = {"GB/s": round(nbytes / (ms_d * 1e-3) / 1e9, 1), "ms_per_call": round(ms_d, 4)}
@@ -425,7 +454,7 @@ def main(argv=None) -> int:
         pnp = pdx.num_pages
         po = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device=dev)
         plse = torch.empty((dc.B, dc.H), dtype=torch.float32, device=dev)
-        pwsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, pmp * page, dc.d, args.splits)
+        pwsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, args.splits)
         pws = torch.empty(pwsb // 4, dtype=torch.float32, device=dev)
         calls["decode_paged"] = lambda: fa.attn_decode_paged(pq, pk, pv, ptab, psl, po, plse, dc.B, dc.H, dc.Hkv, page,
                                                              pmp, pnp, dc.d, dc.scale, args.splits, pws,
@@ -436,7 +465,7 @@ def main(argv=None) -> int:
         dsl = torch.from_numpy(dx.seqlens).to(dev)
         do = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device=dev)
         dlse = torch.empty((dc.B, dc.H), dtype=torch.float32, device=dev)
-        wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, args.splits)
+        wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, args.splits)
         ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
         calls["decode"] = lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
                                                  dc.scale, args.splits, ws, wsb)
@@ -496,7 +525,9 @@ def main(argv=None) -> int:
         step(rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {name: sum(a.elapsed_time(b) for a, b in rec[name]) / max(1, len(rec[name])) for name in parts}
+    per_launch = {name: sorted(a.elapsed_time(b) for a, b in rec[name]) for name in parts}
+    ms = {name: sum(v) / max(1, len(v)) for name, v in per_launch.items()}
+    med = {name: (v[len(v) // 2] if v else float("nan")) for name, v in per_launch.items()}
 
     out = {
         "metric": "attn fwd TFLOPS & % bf16 MFMA peak (N=4096,d=128 causal); decode HBM GB/s",
@@ -515,53 +546,76 @@ def main(argv=None) -> int:
                    "global_batch": pc.B, "seq_len": pc.N, "parallelism": "none (1 GPU)"},
     }
     if "prefill" in parts:
-        flops = 2 * pc.N * pc.N * pc.d * pc.B * pc.H
+        flops = prefill_flops(pc.B, pc.H, pc.N, pc.d, True)
         tflops = flops / (ms["prefill"] * 1e-3) / 1e12
         out["value"] = round(tflops, 2)
         traffic = read_traffic()
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                            "kernel": "tile_kernel<128,causal,softmax>", "flops_per_launch": flops,
-                           "ms_per_launch": round(ms["prefill"], 4)}
+                           "ms_per_launch": round(ms["prefill"], 4), "median_ms_per_launch": round(med["prefill"], 4),
+                           "launches": len(per_launch["prefill"])}
     if "decode" in parts:
         ssum = int(dx.seqlens.sum())
-        nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
+        nbytes = decode_bytes(dx.seqlens, dc.B, dc.H, dc.Hkv, dc.d)
         gbs = nbytes / (ms["decode"] * 1e-3) / 1e9
         out["decode"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                         "ms_per_call": round(ms["decode"], 4), "algorithmic_bytes": nbytes, "sum_L": ssum,
-                         "splits": args.splits or "auto"}
+                         "ms_per_call": round(ms["decode"], 4), "median_ms_per_call": round(med["decode"], 4),
+                         "algorithmic_bytes": nbytes, "sum_L": ssum, "splits": args.splits or "auto"}
+        # the same decode at 16, 32 and 64 chunks per sequence (the automatic
+        # count above is 768 work items in all, 6 chunks per sequence here)
+        sweep = {}
+        swsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, 64)
+        sws = torch.empty(swsb // 4, dtype=torch.float32, device=dev)
+        for sp in (16, 32, 64):
+            ms_s = _time_calls(lambda: fa.attn_decode(dq, dk, dv, dsl, do, dlse, dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d,
+                                                      dc.scale, sp, sws, swsb), stream, reps=20)
+            sweep[str(sp)] = {"GB/s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
+                              "frac_hbm_peak": round(nbytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "ms_per_call": round(ms_s, 4)}
+        out["decode"]["splits_sweep"] = sweep
+        del sws
         if out["value"] is None:
             out.update({"value": round(gbs, 1), "unit": "GB/s"})
     if "decode_paged" in parts:
         ssum = int(dx.seqlens.sum())
         # same algorithmic bytes as the contiguous decode (the block-table reads,
         # 4 bytes per 16-row page, are under 0.01 % and not counted)
-        nbytes = ssum * dc.Hkv * dc.d * 2 * 2 + 2 * dc.B * dc.H * dc.d * 2 + dc.B * dc.H * 4 + dc.B * 4
+        nbytes = decode_bytes(dx.seqlens, dc.B, dc.H, dc.Hkv, dc.d)
         gbs = nbytes / (ms["decode_paged"] * 1e-3) / 1e9
         out["decode_paged"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                               "ms_per_call": round(ms["decode_paged"], 4), "algorithmic_bytes": nbytes,
+                               "ms_per_call": round(ms["decode_paged"], 4),
+                               "median_ms_per_call": round(med["decode_paged"], 4), "algorithmic_bytes": nbytes,
                                "page_size": 16, "splits": args.splits or "auto"}
         if out["value"] is None:
             out.update({"value": round(gbs, 1), "unit": "GB/s"})
     if "hstu" in parts:
-        hf = sum(2 * int(L) * int(L) * jc.d for L in jx.lengths) * jc.H
+        hf = hstu_flops(jx.lengths, jc.H, jc.d)
         ht = hf / (ms["hstu"] * 1e-3) / 1e12
+        # transcendental bound: two per score (exp2 and rcp of the SiLU weight),
+        # scores counted by the same causal convention (flops / 4d)
+        scores = hf / (4 * jc.d)
+        trans_ms = 2 * scores / 64 * TRANS_CYCLES_PER_WAVE_OP / (SIMDS * SPEC_CLOCK_HZ) * 1e3
         out["hstu"] = {"TFLOP/s": round(ht, 2), "frac_bf16_peak": round(ht / PEAK_BF16_TFLOPS, 4),
-                       "ms_per_call": round(ms["hstu"], 4), "flops": hf}
+                       "ms_per_call": round(ms["hstu"], 4), "median_ms_per_call": round(med["hstu"], 4),
+                       "flops": hf, "trans_bound_ms": round(trans_ms, 4),
+                       "frac_trans_bound": round(trans_ms / ms["hstu"], 4)}
         if out["value"] is None:
             out.update({"value": round(ht, 2), "unit": "TFLOP/s"})
     if "backward" in parts:
-        bf = 5 * pc.N * pc.N * pc.d * pc.B * pc.H
+        bf = backward_flops(pc.B, pc.H, pc.N, pc.d, True)
         bt = bf / (ms["backward"] * 1e-3) / 1e12
         out["backward"] = {"TFLOP/s": round(bt, 2), "frac_bf16_peak": round(bt / PEAK_BF16_TFLOPS, 4),
-                           "ms_per_call": round(ms["backward"], 4), "flops": bf}
+                           "ms_per_call": round(ms["backward"], 4), "median_ms_per_call": round(med["backward"], 4),
+                           "flops": bf}
         if out["value"] is None:
             out.update({"value": round(bt, 2), "unit": "TFLOP/s"})
     if "prefill_fp8" in parts:
-        ff = 2 * fc.N * fc.N * fc.d * fc.B * fc.H
+        ff = prefill_flops(fc.B, fc.H, fc.N, fc.d, True)
         ft = ff / (ms["prefill_fp8"] * 1e-3) / 1e12
         out["prefill_fp8"] = {"TFLOP/s": round(ft, 2), "frac_fp8_peak": round(ft / PEAK_FP8_TFLOPS, 4),
-                              "ms_per_call": round(ms["prefill_fp8"], 4), "flops": ff}
+                              "ms_per_call": round(ms["prefill_fp8"], 4),
+                              "median_ms_per_call": round(med["prefill_fp8"], 4), "flops": ff}
         if out["value"] is None:
             out.update({"value": round(ft, 2), "unit": "TFLOP/s"})
     if "hstu_padded" in parts:

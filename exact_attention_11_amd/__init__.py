@@ -82,7 +82,7 @@ _SIGNATURES = {
     "attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
-    "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                _vp]),
@@ -177,9 +177,8 @@ def attn_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, Hkv, N,
     _check("attn_fwd_fp8", st)
 
 
-def attn_decode_workspace_bytes(B, H, Hkv, lmax_hint, d, num_splits) -> int:
-    return int(library().attn_decode_workspace_bytes(int(B), int(H), int(Hkv), int(lmax_hint), int(d),
-                                                     int(num_splits)))
+def attn_decode_workspace_bytes(B, H, d, num_splits) -> int:
+    return int(library().attn_decode_workspace_bytes(int(B), int(H), int(d), int(num_splits)))
 
 
 def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scale, num_splits, workspace,

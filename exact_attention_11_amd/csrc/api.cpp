@@ -162,16 +162,10 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(fattn::launch_tile_fp8(a, static_cast<hipStream_t>(stream)), "attn_fwd_fp8 launch");
 }
 
-size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits) {
-  if (B < 0 || H < 1 || Hkv < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;
-  int s = num_splits;
-  if (s == 0) {
-    if (lmax_hint < 1) return 0;
-    // large enough for either cache layout's automatic count
-    const int sc = fattn::decode_auto_splits(B, Hkv, lmax_hint, false);
-    const int sp = fattn::decode_auto_splits(B, Hkv, lmax_hint, true);
-    s = sc > sp ? sc : sp;
-  }
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+  if (B < 0 || H < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;
+  // the automatic count of either entry point is at most 64 splits
+  const int s = num_splits == 0 ? 64 : num_splits;
   const size_t bytes = (size_t)H * B * (s + 1) * ((size_t)d + 1) * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
@@ -200,7 +194,13 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if ((double)B * Hkv * Lmax * d > 9.0e15) return fail(FATTN_ERR_INVALID_ARG, "%s: cache too large", fn);
   const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax, false) : num_splits;
-  const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
+  // a work item holds at most ceil(ceil(Lmax / 32) / splits) blocks of 32 keys
+  // of 256 bytes each per kv head; its byte offsets are 32-bit
+  const double item_bytes = std::ceil(std::ceil(Lmax / 32.0) / splits) * 32.0 * (d * 2);
+  if (item_bytes >= 4294967296.0)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: a work item of %.0f bytes per kv head passes 32-bit offsets; use more splits",
+                fn, item_bytes);
+  const size_t need = attn_decode_workspace_bytes(B, H, d, splits);
   if (workspace_bytes < need)
     return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
                 workspace_bytes, need);
@@ -262,7 +262,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     return fail(FATTN_ERR_UNSUPPORTED,
                 "%s: one work item could span %d pages (at most %d); use more splits or larger pages",
                 fn, (chunk + page_size - 1) / page_size, fattn::kDecodeMaxSplitPages);
-  const size_t need = attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, splits);
+  const size_t need = attn_decode_workspace_bytes(B, H, d, splits);
   if (workspace_bytes < need)
     return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
                 workspace_bytes, need);

@@ -119,6 +119,15 @@ struct Lds {
   __device__ static __forceinline__ int vswz(int r) { return D >= 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
 };
 
+// Rows [s0, s1) of packed sequence b: offsets[b] and offsets[b + 1] clamped
+// into [0, offsets[B]] with s1 >= s0, so that offsets that are out of order or
+// out of range never address a row outside [0, offsets[B]).
+__device__ __forceinline__ void jagged_rows(const TileArgs& a, int b, int& s0, int& s1) {
+  const int total = max(a.offsets[a.B], 0);
+  s0 = min(max(a.offsets[b], 0), total);
+  s1 = min(max(a.offsets[b + 1], s0), total);
+}
+
 // In-block key order of the first product: swap bits 2 and 3.
 __device__ __forceinline__ int key_perm(int m) { return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -164,8 +173,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   int len;
   long lse_base = 0;
   if constexpr (JAGGED) {
-    const int s0 = a.offsets[b];
-    const int s1 = a.offsets[b + 1];
+    int s0, s1;
+    jagged_rows(a, b, s0, s1);
     len = min(s1 - s0, a.N);
     row_stride = (long)a.H * D;
     const long base = ((long)s0 * a.H + h) * D;
@@ -527,8 +536,9 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   grouped_item(a.B * a.H, nqb, 4, bh, slot);
   const int h = bh % a.H;
   const int b = bh / a.H;
-  const int s0 = a.offsets[b];
-  const int len = min(a.offsets[b + 1] - s0, a.N);
+  int s0, s1;
+  jagged_rows(a, b, s0, s1);
+  const int len = min(s1 - s0, a.N);
   const int q0 = (nqb - 1 - slot) * BMW;  // heaviest blocks first
   if (q0 >= len) return;                  // uniform over the workgroup
   const long rs = (long)a.H * D;           // elements between consecutive rows

@@ -10,10 +10,12 @@
  *
  * Arguments are validated on the host before anything is launched; an
  * invalid call launches nothing and returns a non-zero status.  Values that
- * live in device memory (sequence lengths, offsets) are not read by the host:
- * kernels clamp them to the sizes passed in, so a violated precondition gives
- * unspecified output but no out-of-bounds access.  Kernel faults surface at
- * the caller's next synchronisation.
+ * live in device memory (sequence lengths, block tables, offsets) are not
+ * read by the host: kernels clamp them to the sizes passed in (for the jagged
+ * layout, to the total offsets[B]; see attn_hstu_jagged), so a violated
+ * precondition gives unspecified output but no access outside the sizes the
+ * call describes.  Kernel faults surface at the caller's next
+ * synchronisation.
  *
  * Element types: "bf16" is IEEE-style bfloat16 stored as uint16; "f32" is
  * IEEE binary32.  Every tensor is dense and contiguous in the layout given,
@@ -90,16 +92,15 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  void* stream);
 
 /*
- * attn_decode_workspace_bytes -- device workspace attn_decode needs for this
- * shape: room for one partial output row (f32, d values) and one partial
- * log-sum-exp (f32) per (head, slot), B * (num_splits + 1) slots per head,
- * rounded up to 256 bytes.
- * num_splits == 0 asks for room for the automatic choice, the larger of the
- * counts attn_decode and attn_decode_paged would make for the given Lmax
- * (pass it as lmax_hint; ignored otherwise), so one buffer serves both.
- * Returns 0 for an invalid shape.
+ * attn_decode_workspace_bytes -- device workspace attn_decode and
+ * attn_decode_paged need: room for one partial output row (f32, d values) and
+ * one partial log-sum-exp (f32) per (head, slot), B * (num_splits + 1) slots
+ * per head, rounded up to 256 bytes.  num_splits == 0 asks for room for the
+ * automatic choice of either entry point, which is at most 64 splits.
+ * Returns 0 for an invalid shape (B < 0, H < 1, d < 1, num_splits outside
+ * 0..64).
  */
-size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, int num_splits);
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
 /*
  * attn_decode -- one new query token per sequence against a KV cache,
@@ -126,13 +127,20 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int lmax_hint, int d, 
  *   lse        f32  [B, H]               written, or NULL
  *   H % Hkv == 0 with H/Hkv in {1, 2, 4, 8, 16, 32} (32: multi-query
  *              attention with 32 heads); d == 128; scale finite, >= 0.
- *   num_splits 0 = automatic (about 768 work items in all, 1024 for the
- *              paged cache; raised for very long caches), else
- *              1..64: work items per sequence on average.  The T blocks
+ *   num_splits 0 = automatic, else 1..64: the average number of chunks
+ *              (work items) per sequence.  The T 32-key blocks of the batch
  *              (ceil(seqlens_k[b] / 32) per sequence, summed) are cut into
- *              min(B * num_splits, T) runs of floor/ceil(T / items) blocks.
- *   workspace  device buffer of at least attn_decode_workspace_bytes(...)
- *              bytes for the same arguments; contents on entry are ignored.
+ *              min(B * num_splits, T) equal runs of floor/ceil(T / items)
+ *              blocks, so sequences of equal length get num_splits chunks
+ *              each and longer sequences more.  Automatic: about 768 work
+ *              items in all (1024 for the paged cache), i.e. 768 / (B * Hkv)
+ *              chunks per sequence, at most 64 -- measured faster than a
+ *              fixed 16 on the GQA decode workload -- raised for very long
+ *              caches.  A count whose work items would span 2^32 bytes of one
+ *              kv head returns FATTN_ERR_UNSUPPORTED.
+ *   workspace  device buffer of at least
+ *              attn_decode_workspace_bytes(B, H, d, num_splits) bytes;
+ *              contents on entry are ignored.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens_k, void* o, float* lse,
@@ -160,7 +168,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *   page_size         a power of two in [16, 1024].
  *   q, o, lse, H, Hkv, d, scale, num_splits: as attn_decode, with
  *   Lmax = max_pages_per_seq * page_size.  Workspace: at least
- *   attn_decode_workspace_bytes(B, H, Hkv, Lmax, d, num_splits) bytes.
+ *   attn_decode_workspace_bytes(B, H, d, num_splits) bytes.
  *   A split may span at most 2047 pages; a call whose splits would span more
  *   returns FATTN_ERR_UNSUPPORTED (use more splits or larger pages).
  */
@@ -190,7 +198,12 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
  *   q, k, v   bf16 [T, H, d] packed: sequence b owns rows
  *             [offsets[b], offsets[b+1])
  *   o         bf16 [T, H, d]  written (rows of every sequence)
- *   offsets   int32 [B + 1], device memory, non-decreasing, offsets[0] = 0
+ *   offsets   int32 [B + 1], device memory, non-decreasing, offsets[0] = 0,
+ *             offsets[B] = T.  The kernels read offsets[B] as the row count
+ *             and clamp every offsets[b] into [0, offsets[B]] and every
+ *             length to >= 0, so no row outside [0, offsets[B]) is touched;
+ *             offsets[B] itself must not exceed the rows of q, k, v and o
+ *             (the library cannot check it).
  *   max_seqlen >= every sequence length (rows beyond it are not computed)
  *   d in {64, 128}; alpha, inv_n finite; causal in {0, 1} (1: key j <= row i).
  */

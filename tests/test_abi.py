@@ -90,7 +90,7 @@ def test_empty_calls_launch_nothing(fn):
 
 def _dec(**kw):
     B, H, Hkv, L, d = 2, 8, 2, 100, 128
-    ws = fa.attn_decode_workspace_bytes(B, H, Hkv, L, d, 0)
+    ws = fa.attn_decode_workspace_bytes(B, H, d, 0)
     args = dict(q=P, k_cache=P, v_cache=P, seqlens_k=P, o=P, lse=None, B=B, H=H, Hkv=Hkv, Lmax=L, d=d, scale=0.1,
                 num_splits=0, workspace=P, workspace_bytes=ws)
     args.update(kw)
@@ -120,18 +120,22 @@ def test_attn_decode_rejects(kw, status):
 def test_decode_workspace_size():
     # one f32 row of d plus one f32 LSE per (head, slot), B * (splits + 1)
     # slots per head, rounded to 256 B
-    assert fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 64) == 32 * 16 * 65 * 129 * 4
-    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 1) == 1280  # 1032 -> 1280
-    # automatic split count for Lmax = 1 is one split: 8256 bytes -> 8448
-    assert fa.attn_decode_workspace_bytes(2, 4, 2, 1, 128, 0) == 8448
-    auto = fa.attn_decode_workspace_bytes(16, 32, 8, 32768, 128, 0)
-    # 16 x 8 (sequence, kv-head) pairs: 6 splits (768 items) contiguous, 8 (1024) paged; room for 8
-    assert auto == 32 * 16 * 9 * 129 * 4
-    # a long cache raises the automatic count so that no work item spans more
-    # than 2047 pages of 16 keys: Lmax = 10^6 -> ceil(10^6 / 32736) = 31 splits
-    assert fa.attn_decode_workspace_bytes(16, 32, 8, 1_000_000, 128, 0) == 32 * 16 * 32 * 129 * 4
-    assert fa.attn_decode_workspace_bytes(1, 1, 1, 10, 128, 65) == 0
-    assert fa.attn_decode_workspace_bytes(1, 0, 1, 10, 128, 1) == 0
+    assert fa.attn_decode_workspace_bytes(16, 32, 128, 64) == 32 * 16 * 65 * 129 * 4
+    assert fa.attn_decode_workspace_bytes(1, 1, 128, 1) == 1280  # 1032 -> 1280
+    assert fa.attn_decode_workspace_bytes(2, 4, 128, 3) == 16640  # 16512 -> 16640
+    # num_splits = 0 (automatic): room for the largest automatic count, 64
+    assert fa.attn_decode_workspace_bytes(16, 32, 128, 0) == fa.attn_decode_workspace_bytes(16, 32, 128, 64)
+    assert fa.attn_decode_workspace_bytes(1, 1, 128, 65) == 0
+    assert fa.attn_decode_workspace_bytes(1, 0, 128, 1) == 0
+    assert fa.attn_decode_workspace_bytes(-1, 1, 128, 1) == 0
+
+
+def test_decode_rejects_work_items_beyond_32_bit_offsets():
+    # one split over 2^25 keys of 256 bytes: a work item's byte offsets would
+    # pass 2^32; the call is refused before anything is launched
+    with pytest.raises(fa.FattnError) as e:
+        _dec(Lmax=1 << 25, num_splits=1)
+    assert e.value.status == fa.FATTN_ERR_UNSUPPORTED
 
 
 def _hstu(**kw):
@@ -163,7 +167,7 @@ def test_hstu_empty_calls_launch_nothing():
 
 def _paged(**kw):
     B, H, Hkv, psz, mp, d = 2, 8, 2, 16, 8, 128
-    ws = fa.attn_decode_workspace_bytes(B, H, Hkv, psz * mp, d, 0)
+    ws = fa.attn_decode_workspace_bytes(B, H, d, 0)
     args = dict(q=P, k_pages=P, v_pages=P, block_table=P, seqlens_k=P, o=P, lse=None, B=B, H=H,
                 Hkv=Hkv, page_size=psz, max_pages_per_seq=mp, num_pages=64, d=d, scale=0.1, num_splits=0,
                 workspace=P, workspace_bytes=ws)

@@ -4,7 +4,8 @@ fp64 oracle's gradients.
 The forward output and LSE that the backward consumes come from ``attn_fwd``
 on the GPU (the product path's own data flow); the oracle computes the
 gradients from q, k, v and dO alone.  Small cases compare every element over
-several tiles with ragged tails; the full-size case compares whole heads.
+several tiles with ragged tails; the full-size case compares every element
+of two whole batches.
 """
 
 import math
@@ -106,24 +107,22 @@ def test_bwd_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-def test_bwd_full_size_causal_heads():
-    """B=8, H=32, N=4096, d=128 causal (the prefill benchmark shape): whole
-    heads compared, three of them, in the launch configuration the benchmark
-    times."""
+@pytest.mark.timeout(600)
+def test_bwd_full_size_causal_two_batches():
+    """B=8, H=32, N=4096, d=128 causal (the prefill benchmark shape), in the
+    launch configuration the benchmark times: every element of dQ, dK and dV
+    of batches 0 and 7 (all 32 heads of each)."""
     _need_gpu()
     c = W.PREFILL_D128_CAUSAL
     x = W.dense_inputs(c)
     do = normal_bf16(c.seed, TENSOR_DO, (c.B, c.H, c.N, c.d))
     dq, dk, dv = run_bwd(x.q, x.k, x.v, do, c.B, c.H, c.Hkv, c.N, c.d, c.scale, 1)
-    group = c.H // c.Hkv
-    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
-        g = h // group
-        hs = slice(g * group, (g + 1) * group)
-        rq, rk, rv = oracle.attention_backward(
-            x.f64("q", (slice(b, b + 1), hs)), x.f64("k", (slice(b, b + 1), slice(g, g + 1))),
-            x.f64("v", (slice(b, b + 1), slice(g, g + 1))), bf16_bits_to_f64(do[b:b + 1, hs]), c.scale, True)
-        assert_grad(bf16_dev_to_f64(dq[b, hs]), rq[0], f"dQ b={b} h={h}")
-        assert_grad(bf16_dev_to_f64(dk[b, g]), rk[0, 0], f"dK b={b} g={g}")
-        assert_grad(bf16_dev_to_f64(dv[b, g]), rv[0, 0], f"dV b={b} g={g}")
     for t in (dq, dk, dv):
-        assert torch.isfinite(t[:, :, ::61].float()).all()
+        assert torch.isfinite(t.float()).all()
+    for b in (0, 7):
+        bs = slice(b, b + 1)
+        rq, rk, rv = oracle.attention_backward(x.f64("q", (bs,)), x.f64("k", (bs,)), x.f64("v", (bs,)),
+                                               bf16_bits_to_f64(do[bs]), c.scale, True)
+        assert_grad(bf16_dev_to_f64(dq[b]), rq[0], f"dQ b={b}")
+        assert_grad(bf16_dev_to_f64(dk[b]), rk[0], f"dK b={b}")
+        assert_grad(bf16_dev_to_f64(dv[b]), rv[0], f"dV b={b}")

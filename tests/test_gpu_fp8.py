@@ -12,7 +12,7 @@ import oracle
 from synthgen import bf16_bits_to_f64
 from synthgen import workloads as W
 
-from _util import assert_fp8, assert_lse, sample_rows
+from _util import assert_fp8, assert_lse
 
 pytestmark = pytest.mark.gpu
 
@@ -61,17 +61,27 @@ def test_fp8_per_head_descales_are_applied():
     assert_lse(lse, L_ref, "per-head descales")
 
 
-def test_fp8_full_size_sampled_rows():
-    """B=8, H=32, N=4096, d=128 causal in FP8: sampled rows of three heads."""
+_FP8_FULL = {}
+
+
+def _fp8_full():
+    """Inputs and GPU outputs of the full-size FP8 workload, run once."""
+    if not _FP8_FULL:
+        x = W.fp8_dense_inputs(W.PREFILL_FP8)
+        o, lse = run_fp8(x)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        _FP8_FULL["run"] = (x, o, lse)
+    return _FP8_FULL["run"]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("b", range(8))
+def test_fp8_full_size_every_element(b):
+    """B=8, H=32, N=4096, d=128 causal in FP8: every element of batch b."""
     _need_gpu()
     c = W.PREFILL_FP8
-    x = W.fp8_dense_inputs(c)
-    o, lse = run_fp8(x)
-    rows = sample_rows(c.N)
-    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
-        idx = (slice(b, b + 1), slice(h, h + 1))
-        O_ref, L_ref = oracle.attention_forward(x.f64("q", idx), x.f64("k", idx), x.f64("v", idx), c.scale, True,
-                                                rows=rows)
-        assert_fp8(o[b, h, rows], O_ref[0, 0], f"b={b} h={h}")
-        assert_lse(lse[b, h, rows], L_ref[0, 0], f"b={b} h={h}")
-    assert np.isfinite(o[:, :, ::97]).all() and np.isfinite(lse).all()
+    x, o, lse = _fp8_full()
+    idx = (slice(b, b + 1),)
+    O_ref, L_ref = oracle.attention_forward(x.f64("q", idx), x.f64("k", idx), x.f64("v", idx), c.scale, True)
+    assert_fp8(o[b], O_ref[0], f"b={b}")
+    assert_lse(lse[b], L_ref[0], f"b={b}")

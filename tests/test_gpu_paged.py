@@ -36,7 +36,7 @@ def run_paged(px: W.PagedDecodeInputs, splits: int):
     table, sl = to_dev(px.block_table), to_dev(x.seqlens)
     o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
-    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, mp * px.page_size, c.d, splits)
+    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.d, splits)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     fa.attn_decode_paged(q, kp, vp, table, sl, o, lse, c.B, c.H, c.Hkv, px.page_size, mp, px.num_pages, c.d,
                          c.scale, splits, ws, nbytes)
@@ -49,7 +49,7 @@ def run_contiguous(x: W.DecodeInputs, splits: int, Lmax: int):
     q, k, v = to_dev_bf16(x.q), to_dev_bf16(x.k), to_dev_bf16(x.v)
     o = torch.empty((c.B, c.H, c.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
-    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.Hkv, Lmax, c.d, splits)
+    nbytes = fa.attn_decode_workspace_bytes(c.B, c.H, c.d, splits)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     fa.attn_decode(q, k, v, to_dev(x.seqlens), o, lse, c.B, c.H, c.Hkv, c.Lmax, c.d, c.scale, splits, ws, nbytes)
     torch.cuda.synchronize()
@@ -147,7 +147,7 @@ def test_paged_auto_splits_with_a_long_page_table():
     q, kp, vp = to_dev_bf16(x.q), to_dev_bf16(px.k_pages), to_dev_bf16(px.v_pages)
     o = torch.empty((B, 1, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, 1), dtype=torch.float32, device="cuda")
-    nbytes = fa.attn_decode_workspace_bytes(B, 1, 1, wide * P, 128, 0)
+    nbytes = fa.attn_decode_workspace_bytes(B, 1, 128, 0)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     fa.attn_decode_paged(q, kp, vp, to_dev(table), to_dev(x.seqlens), o, lse, B, 1, 1, P, wide, px.num_pages, 128,
                          c.scale, 0, ws, nbytes)

@@ -94,7 +94,7 @@ def test_random_decode_contiguous_and_paged(i):
         L_ref.append(Lb[0])
     O_ref, L_ref = np.stack(O_ref), np.stack(L_ref)
     # contiguous
-    nbytes = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, c["splits"])
+    nbytes = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, c["splits"])
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     o = torch.empty((dc.B, dc.H, dc.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((dc.B, dc.H), dtype=torch.float32, device="cuda")
@@ -107,7 +107,7 @@ def test_random_decode_contiguous_and_paged(i):
     # paged (shuffled pages, NaN spare pages and tails), bitwise equal to contiguous
     px = W.paged_from_decode(x, c["page"], perm_seed=i)
     mp = px.block_table.shape[1]
-    nbytes = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, mp * c["page"], dc.d, c["splits"])
+    nbytes = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, c["splits"])
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     po = torch.empty_like(o)
     plse = torch.empty_like(lse)

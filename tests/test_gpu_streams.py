@@ -52,7 +52,7 @@ def test_two_streams_match_serial_calls_bitwise():
             "ho": torch.empty((T, jc.H, jc.d), dtype=torch.bfloat16, device="cuda"),
         }
 
-    wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.Hkv, dc.Lmax, dc.d, 0)
+    wsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, 0)
 
     def prefill(out, stream=None):
         fa.attn_fwd(pq, pk, pv, out["o"], out["lse"], pc.B, pc.H, pc.Hkv, pc.N, pc.d, pc.scale, 1, stream)
