@@ -23,6 +23,7 @@ __all__ = [
     "attn_fwd_fp8",
     "attn_decode",
     "attn_decode_workspace_bytes",
+    "attn_decode_noalloc",
     "attn_decode_paged",
     "attn_hstu_jagged",
     "attn_bwd",
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "attn_fwd_fp8",
     "attn_decode_workspace_bytes",
     "attn_decode",
+    "attn_decode_noalloc",
     "attn_decode_paged",
     "attn_hstu_jagged",
     "attn_bwd_workspace_bytes",
@@ -84,6 +86,7 @@ _SIGNATURES = {
     "attn_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                _vp]),
     "attn_hstu_jagged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _f, _i, _vp]),
@@ -188,6 +191,15 @@ def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scal
                                int(B), int(H), int(Hkv), int(Lmax), int(d), float(scale), int(num_splits),
                                _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("attn_decode", st)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scale, num_splits, stream=None):
+    """attn_decode with the library's static scratch array as its workspace;
+    see ``attn_decode_noalloc`` in include/fattn.h."""
+    st = library().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o), _ptr(lse),
+                                       int(B), int(H), int(Hkv), int(Lmax), int(d), float(scale), int(num_splits),
+                                       _stream(stream))
+    _check("attn_decode_noalloc", st)
 
 
 def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, o, lse, B, H, Hkv, page_size, max_pages_per_seq,

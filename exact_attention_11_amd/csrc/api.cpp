@@ -170,10 +170,18 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   return (bytes + 255) / 256 * 256;
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k, void* o,
-                float* lse, int B, int H, int Hkv, int Lmax, int d, float scale, int num_splits, void* workspace,
-                size_t workspace_bytes, void* stream) {
-  const char* fn = "attn_decode";
+}  // extern "C"
+
+namespace {
+
+// Validation shared by attn_decode and attn_decode_noalloc: every argument
+// except the workspace; on success `a` is filled except part_o / part_lse and
+// `need` holds the workspace bytes the call uses.  `*done` is set when the
+// call has nothing to launch (B == 0).
+int prepare_decode(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Hkv, int Lmax, int d, float scale,
+                   int num_splits, fattn::DecodeArgs& a, size_t& need, bool* done) {
+  *done = false;
   if (B < 0) return fail(FATTN_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
   if (H < 1 || Hkv < 1) return fail(FATTN_ERR_INVALID_ARG, "%s: H and Hkv must be >= 1", fn);
   if (H % Hkv != 0) return fail(FATTN_ERR_INVALID_ARG, "%s: H=%d is not a multiple of Hkv=%d", fn, H, Hkv);
@@ -186,11 +194,13 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   if (d != 128) return fail(FATTN_ERR_UNSUPPORTED, "%s: d=%d not supported (128)", fn, d);
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16 && G != 32)
     return fail(FATTN_ERR_UNSUPPORTED, "%s: H/Hkv=%d not supported (1, 2, 4, 8, 16 or 32)", fn, G);
-  if (B == 0) return ok();
-  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !workspace)
-    return fail(FATTN_ERR_INVALID_ARG, "%s: q, caches, seqlens_k, o and workspace must be non-null", fn);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace) ||
-      (lse && !aligned16(lse)))
+  if (B == 0) {
+    *done = true;
+    return FATTN_OK;
+  }
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: q, caches, seqlens_k and o must be non-null", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || (lse && !aligned16(lse)))
     return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if ((double)B * Hkv * Lmax * d > 9.0e15) return fail(FATTN_ERR_INVALID_ARG, "%s: cache too large", fn);
   const int splits = num_splits == 0 ? fattn::decode_auto_splits(B, Hkv, Lmax, false) : num_splits;
@@ -200,11 +210,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   if (item_bytes >= 4294967296.0)
     return fail(FATTN_ERR_UNSUPPORTED, "%s: a work item of %.0f bytes per kv head passes 32-bit offsets; use more splits",
                 fn, item_bytes);
-  const size_t need = attn_decode_workspace_bytes(B, H, d, splits);
-  if (workspace_bytes < need)
-    return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
-                workspace_bytes, need);
-  fattn::DecodeArgs a{};
+  need = attn_decode_workspace_bytes(B, H, d, splits);
+  a = fattn::DecodeArgs{};
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -218,9 +225,58 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
   a.d = d;
   a.c = scale * kLog2e;
   a.splits = splits;
+  return FATTN_OK;
+}
+
+void set_decode_workspace(fattn::DecodeArgs& a, void* workspace) {
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + (size_t)H * B * (splits + 1) * d;
+  a.part_lse = a.part_o + (size_t)a.H * a.B * (a.splits + 1) * a.d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k, void* o,
+                float* lse, int B, int H, int Hkv, int Lmax, int d, float scale, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const char* fn = "attn_decode";
+  fattn::DecodeArgs a;
+  size_t need = 0;
+  bool done = false;
+  const int st = prepare_decode(fn, q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scale, num_splits, a,
+                                need, &done);
+  if (st != FATTN_OK) return st;
+  if (done) return ok();
+  if (!workspace) return fail(FATTN_ERR_INVALID_ARG, "%s: workspace must be non-null", fn);
+  if (!aligned16(workspace)) return fail(FATTN_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(FATTN_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                workspace_bytes, need);
+  set_decode_workspace(a, workspace);
   return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k, void* o,
+                        float* lse, int B, int H, int Hkv, int Lmax, int d, float scale, int num_splits,
+                        void* stream) {
+  const char* fn = "attn_decode_noalloc";
+  fattn::DecodeArgs a;
+  size_t need = 0;
+  bool done = false;
+  const int st = prepare_decode(fn, q, k_cache, v_cache, seqlens_k, o, lse, B, H, Hkv, Lmax, d, scale, num_splits, a,
+                                need, &done);
+  if (st != FATTN_OK) return st;
+  if (done) return ok();
+  if (need > fattn::kDecodeScratchBytes)
+    return fail(FATTN_ERR_UNSUPPORTED, "%s: the call needs %zu bytes of workspace, more than the %zu of the static "
+                "scratch array; use fewer splits or attn_decode with a workspace", fn, need,
+                (size_t)fattn::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = fattn::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "attn_decode_noalloc scratch lookup");
+  set_decode_workspace(a, scratch);
+  return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_noalloc launch");
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,

@@ -24,6 +24,9 @@
 //  * kernel 2, one workgroup per (sequence, head): weights exp(lse_c - lse)
 //    with lse = log-sum-exp over the sequence's partials, O = sum_c w_c o_c;
 //    an empty sequence gives O = 0 and LSE = -inf.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -471,6 +474,41 @@ int decode_auto_splits(int B, int Hkv, int Lmax, bool paged) {
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;
+}
+
+// Decode workspace for callers that cannot allocate (attn_decode_noalloc):
+// kDecodeScratchBytes per device, held until the process ends.  In host code
+// the name `scratch` stands for the array but is not its device address; the
+// address is looked up once per device with that device current and only that
+// address is passed to kernels.  Every call on one device shares the array:
+// calls that overlap on a device race.  Its contents on entry do not matter
+// (the split kernel writes every slot the combine reads), so nothing clears it.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

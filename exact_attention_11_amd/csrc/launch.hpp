@@ -74,6 +74,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Automatic split count for a decode shape (contiguous or paged cache).
 int decode_auto_splits(int B, int Hkv, int Lmax, bool paged);
 
+// Size of the static decode scratch array (one per device, for callers that
+// cannot allocate a workspace).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// Device address of the current device's decode scratch array, looked up
+// (hipGetSymbolAddress) on the first call on each device and kept.
+hipError_t decode_scratch(void** ptr);
+
 struct Fp8Args {
   const void* q;            // [B, H, N, d] E4M3
   const void* k;            // [B, Hkv, N, d] E4M3

@@ -149,6 +149,27 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode without a caller-supplied workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The partials live
+ * in a static device array of 32 MiB per GPU that the library owns and keeps
+ * until the process ends; the call itself allocates nothing.
+ *
+ *   Arguments as attn_decode, without workspace and workspace_bytes.
+ *   A call whose workspace, attn_decode_workspace_bytes(B, H, d, splits) for
+ *   the split count it uses, exceeds 32 MiB returns FATTN_ERR_UNSUPPORTED
+ *   (use fewer splits, or attn_decode).  The first call on each device looks
+ *   up the array's device address (hipGetSymbolAddress) with that device
+ *   current.  All calls on one device share the array: calls that may overlap
+ *   on one device (several streams, several host threads) race and must be
+ *   ordered by the caller.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, void* o, float* lse,
+                        int B, int H, int Hkv, int Lmax, int d, float scale,
+                        int num_splits, void* stream);
+
+/*
  * attn_decode_paged -- attn_decode over a paged KV cache.
  *
  * The cache lives in fixed-size pages found through a per-sequence block

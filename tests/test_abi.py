@@ -242,3 +242,19 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "libfattn.so"))
     with pytest.raises(fa.FattnLibraryError):
         fa.library()
+
+
+def test_decode_noalloc_rejects_before_launch():
+    # invalid arguments, as attn_decode
+    with pytest.raises(fa.FattnError) as e:
+        fa.attn_decode_noalloc(0, P, P, P, P, None, 2, 8, 2, 100, 128, 0.1, 0, stream=S0)
+    assert e.value.status == fa.FATTN_ERR_INVALID_ARG
+    # a workspace beyond the 32 MiB static array: B=64, H=64, 64 splits need
+    # 64 * 64 * 65 * 129 * 4 bytes
+    assert fa.attn_decode_workspace_bytes(64, 64, 128, 64) > 32 << 20
+    with pytest.raises(fa.FattnError) as e:
+        fa.attn_decode_noalloc(P, P, P, P, P, None, 64, 64, 8, 4096, 128, 0.1, 64, stream=S0)
+    assert e.value.status == fa.FATTN_ERR_UNSUPPORTED
+    assert "32" in fa.fattn_last_error() or "scratch" in fa.fattn_last_error()
+    # B == 0 is a valid empty call
+    fa.attn_decode_noalloc(0, 0, 0, 0, 0, None, 0, 8, 2, 100, 128, 0.1, 0, stream=S0)
