@@ -513,8 +513,48 @@ hipError_t launch_causal(const TileArgs& a, hipStream_t s) {
 // order at the end, so results do not depend on timing; with the tiles split
 // by parity, zero-padded keys past a sequence only add exact zeros to either
 // sum, so a zero-padded batch gives the jagged result bit for bit.
+// Work item of a jagged launch balanced over the 8 XCDs (blockIdx % 8 is the
+// XCD a workgroup is dispatched to).  The (sequence, head) pairs are ranked by
+// sequence length, longest first (ties by index), and dealt to the XCDs in
+// snake order -- ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs 7..0, and so
+// on -- so every XCD gets a near-equal share of the quadratic work while all
+// query blocks of a pair stay on one XCD (its K and V in that XCD's L2).  Each
+// XCD dispatches the query blocks of all its pairs heaviest first: rank u
+// within the XCD is block nqb - 1 - u / n_x of its pair u % n_x.  One lane per
+// sequence ranks the lengths: B <= 64.  The grid is 8 * ceil(B*H / 8) * nqb;
+// a workgroup past its XCD's items returns false.
+__device__ __forceinline__ bool balanced_jagged_item(const TileArgs& a, int nqb, int& b, int& h, int& qb) {
+  const int lane = threadIdx.x & 63;
+  int len = -1;  // lanes past the batch rank after every sequence
+  if (lane < a.B) {
+    int s0, s1;
+    jagged_rows(a, lane, s0, s1);
+    len = min(s1 - s0, a.N);
+  }
+  int rank = 0;  // sequences before this one: longer, or as long with a smaller index
+  for (int t = 0; t < a.B; ++t) {
+    const int lt = __builtin_amdgcn_readlane(len, t);
+    rank += (lt > len || (lt == len && t < lane)) ? 1 : 0;
+  }
+  const int npairs = a.B * a.H;
+  const int x = blockIdx.x & 7, u = blockIdx.x >> 3;
+  // sorted pair i = 8 r + (r even ? x : 7 - x) belongs to XCD x; rows r < full
+  // are complete, row `full` holds the pairs below npairs
+  const int full = npairs >> 3, rem = npairs & 7;
+  const int n_x = full + ((((full & 1) ? 7 - x : x) < rem) ? 1 : 0);
+  if (n_x == 0) return false;
+  const int blk = u / n_x, j = u - blk * n_x;
+  if (blk >= nqb) return false;
+  const int i = 8 * j + ((j & 1) ? 7 - x : x);
+  const int srank = i / a.H;
+  h = i - srank * a.H;
+  b = __builtin_ctzll(__ballot(lane < a.B && rank == srank));
+  qb = nqb - 1 - blk;
+  return true;
+}
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int nqb) {
+__global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int nqb, int balanced) {
   constexpr int D = 64;
   constexpr int BN = 32;
   constexpr int BMW = 64;      // query rows per workgroup
@@ -532,15 +572,21 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
-  int slot, bh;
-  grouped_item(a.B * a.H, nqb, 4, bh, slot);
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  int b, h, qb;
+  if (balanced) {
+    if (!balanced_jagged_item(a, nqb, b, h, qb)) return;  // uniform over the workgroup
+  } else {
+    int slot, bh;
+    grouped_item(a.B * a.H, nqb, 4, bh, slot);
+    h = bh % a.H;
+    b = bh / a.H;
+    qb = nqb - 1 - slot;  // heaviest blocks first
+  }
   int s0, s1;
   jagged_rows(a, b, s0, s1);
   const int len = min(s1 - s0, a.N);
-  const int q0 = (nqb - 1 - slot) * BMW;  // heaviest blocks first
-  if (q0 >= len) return;                  // uniform over the workgroup
+  const int q0 = qb * BMW;
+  if (q0 >= len) return;  // uniform over the workgroup
   const long rs = (long)a.H * D;           // elements between consecutive rows
   const long base = ((long)s0 * a.H + h) * D;
   const uint16_t* qp = (const uint16_t*)a.q + base;
@@ -572,15 +618,24 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   const uint32_t row_bytes = (uint32_t)rs * 2;
   const int lrow = tid >> 3, lch = tid & 7;
   const uint32_t goff = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16u;
+  // one descriptor per tensor over rows [0, len) of this head: rows past the
+  // sequence end read as zero
+  const uint32_t seq_bytes = (uint32_t)(len - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, seq_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, seq_bytes);
   u32x4 kr[2], vr[2];
   auto load_step = [&](int t) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int ti = 2 * t + st;
-      const int k0 = ti * BN;
-      const uint32_t bytes = (ti < n_tiles && k0 < len) ? (uint32_t)(len - k0 - 1) * row_bytes + D * 2 : 0u;
-      kr[st] = buf_load16(make_rsrc(kp + (long)(bytes ? k0 : 0) * rs, bytes), goff);
-      vr[st] = buf_load16(make_rsrc(vp + (long)(bytes ? k0 : 0) * rs, bytes), goff);
+      if (ti < n_tiles) {
+        const uint32_t off = (uint32_t)ti * (BN * row_bytes) + goff;
+        kr[st] = buf_load16(rk, off);
+        vr[st] = buf_load16(rv, off);
+      } else {
+        kr[st] = u32x4{0u, 0u, 0u, 0u};
+        vr[st] = kr[st];
+      }
     }
   };
   auto store_step = [&](int buf) {
@@ -691,10 +746,15 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 template <bool CAUSAL>
 hipError_t launch_hstu_split(const TileArgs& a, hipStream_t stream) {
   const int nqb = (a.N + 63) / 64;
-  const long grid = (long)nqb * a.H * a.B;
+  // XCD-balanced order when one wave can rank the sequences and there are
+  // enough (sequence, head) pairs for every XCD
+  const long npairs = (long)a.H * a.B;
+  const int balanced = (a.B <= 64 && npairs >= 8) ? 1 : 0;
+  const long grid = balanced ? 8L * ((npairs + 7) / 8) * nqb : (long)nqb * npairs;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((hstu_split_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nqb);
+  hipLaunchKernelGGL((hstu_split_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a, nqb,
+                     balanced);
   return hipGetLastError();
 }
 
