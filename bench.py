@@ -28,6 +28,8 @@ Other modes (used for profiling, see profiles/):
                                HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE
                                runs, calibrated by the same counters on a 1 GiB copy
   --traffic-kernel NAME        with --traffic: those bytes for the named kernel(s) instead
+  --counters DIR... --counter-kernel NAME [--counter-trace DIR]
+                               counters of one kernel from --pmc runs, with derived utilisation
 """
 
 from __future__ import annotations
@@ -98,7 +100,9 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["prefill", "decode", "hstu", "backward", "decode_paged", "hstu_padded",
-                                       "prefill_fp8"], default=None)
+                                       "prefill_fp8", "prefill_d64"], default=None,
+                    help="run one part (prefill_d64, the B=1 H=32 N=4096 d=64 causal prefill, is a profiling "
+                         "mode outside the default step)")
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -108,6 +112,10 @@ def parse_args(argv=None):
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--counters", nargs="+", metavar="DIR", help="summarise --pmc runs of one kernel (with "
+                    "--counter-kernel; optional --counter-trace DIR of a --kernel-trace run)")
+    ap.add_argument("--counter-kernel", metavar="NAME")
+    ap.add_argument("--counter-trace", metavar="DIR")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
     ap.add_argument("--traffic-kernel", action="append", default=None, metavar="NAME",
                     help="with --traffic: report this kernel (substring of its name) instead of the prefill; "
@@ -186,6 +194,53 @@ def _pmc_mean_kib(d: str, kernel_substr: str, counter: str) -> float:
     if not vals:
         raise SystemExit(f"no {counter} for {kernel_substr!r} under {d}")
     return sum(vals.values()) / len(vals)
+
+
+def counters_report(dirs, kernel_substr: str, trace_dir=None) -> None:
+    """Counters of one kernel (mean per dispatch over every --pmc run under
+    `dirs`) and what follows from them: MFMA busy fraction, instructions per
+    MFMA, the shader clock from the fastest traced dispatch."""
+    vals = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = {}
+            for r in _read_csv(path):
+                if kernel_substr in r.get("Kernel_Name", ""):
+                    key = (r["Counter_Name"], r.get("Dispatch_Id", ""))
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            by_ctr = {}
+            for (ctr, _), v in per.items():
+                by_ctr.setdefault(ctr, []).append(v)
+            for ctr, v in by_ctr.items():
+                vals[ctr] = sum(v) / len(v)
+    if not vals:
+        raise SystemExit(f"no counters for {kernel_substr!r}")
+    for k in sorted(vals):
+        print(f"{k:28s} {vals[k]:.4g}")
+    print("# derived (GRBM_GUI_ACTIVE is summed over the 8 XCDs; 1024 SIMDs)")
+    gui = vals.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+    mfma = vals.get("SQ_INSTS_MFMA", float("nan"))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        print(f"mfma_busy_fraction           {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.3f}")
+        print(f"mfma_busy_cycles_per_mfma    {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.1f}")
+    for ctr, label in (("SQ_INSTS_VALU", "valu_non_mfma_per_mfma"), ("SQ_INSTS_SALU", "salu_per_mfma"),
+                       ("SQ_INSTS_LDS", "lds_per_mfma"), ("SQ_INSTS_VMEM", "vmem_per_mfma"),
+                       ("SQ_INSTS_VALU_TRANS_F32", "trans_per_mfma")):
+        if ctr in vals:
+            v = vals[ctr] - (mfma if ctr == "SQ_INSTS_VALU" else 0)
+            print(f"{label:28s} {v / mfma:.2f}")
+    if "SQ_BUSY_CYCLES" in vals:
+        # SQ_BUSY_CYCLES is summed over the 32 shader engines
+        print(f"sq_busy_fraction             {vals['SQ_BUSY_CYCLES'] / 32 / gui:.3f}   (SQ_BUSY_CYCLES / 32 SEs)")
+    if "SQ_WAVE_CYCLES" in vals:
+        print(f"mean_resident_waves          {vals['SQ_WAVE_CYCLES'] * 4 / gui:.0f}   (SQ_WAVE_CYCLES counts 4-cycle units)")
+    if trace_dir:
+        for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+            ds = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in _read_csv(path)
+                        if kernel_substr in r.get("Kernel_Name", ""))
+            if ds:
+                print(f"dispatch_us                  {' '.join(f'{x / 1e3:.1f}' for x in ds)}   (kernel-trace run)")
+                print(f"gpu_clock_ghz                {gui / ds[0]:.2f}   (GRBM_GUI_ACTIVE per XCD / fastest dispatch)")
 
 
 PREFILL_KERNEL = "tile_kernel<128, true, (fattn::Epilogue)0, false>"
@@ -372,6 +427,9 @@ def main(argv=None) -> int:
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
         return 0
+    if args.counters:
+        counters_report(args.counters, args.counter_kernel or "", args.counter_trace)
+        return 0
     if args.traffic:
         traffic_summary(*args.traffic, kernels=args.traffic_kernel)
         return 0
@@ -429,6 +487,15 @@ def main(argv=None) -> int:
         calls["prefill"]()  # the backward reads the forward's O and LSE
         calls["backward"] = lambda: fa.attn_bwd(q, k, v, o, lse, gout, gq, gk, gv, pc.B, pc.H, pc.Hkv, pc.N, pc.d,
                                                 pc.scale, 1, bws, bwsb)
+    if "prefill_d64" in parts:
+        c64 = W.PREFILL_D64
+        x64 = W.dense_inputs(c64)
+        q64, k64, v64 = bf16(x64.q), bf16(x64.k), bf16(x64.v)
+        del x64
+        o64 = torch.empty_like(q64)
+        l64 = torch.empty((c64.B, c64.H, c64.N), dtype=torch.float32, device=dev)
+        calls["prefill_d64"] = lambda: fa.attn_fwd(q64, k64, v64, o64, l64, c64.B, c64.H, c64.Hkv, c64.N, c64.d,
+                                                   c64.scale, 1)
     if "prefill_fp8" in parts:
         fc = W.PREFILL_FP8
         fx = W.fp8_dense_inputs(fc)
@@ -618,6 +685,13 @@ def main(argv=None) -> int:
                               "median_ms_per_call": round(med["prefill_fp8"], 4), "flops": ff}
         if out["value"] is None:
             out.update({"value": round(ft, 2), "unit": "TFLOP/s"})
+    if "prefill_d64" in parts:
+        f64_ = prefill_flops(c64.B, c64.H, c64.N, c64.d, True)
+        t64 = f64_ / (ms["prefill_d64"] * 1e-3) / 1e12
+        out["prefill_d64"] = {"TFLOP/s": round(t64, 2), "frac_bf16_peak": round(t64 / PEAK_BF16_TFLOPS, 4),
+                              "ms_per_call": round(ms["prefill_d64"], 4), "flops": f64_}
+        if out["value"] is None:
+            out.update({"value": round(t64, 2), "unit": "TFLOP/s"})
     if "hstu_padded" in parts:
         out["hstu_padded"] = {"ms_per_call": round(ms["hstu_padded"], 4), "padded_to": jc.len_hi,
                               "sequences": len(jx.lengths)}
