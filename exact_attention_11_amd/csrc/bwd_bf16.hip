@@ -328,14 +328,24 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
     toff[i] = (uint32_t)r * ROW + (uint32_t)(pc ^ swz_kv<D>(r)) * 16u;
   }
   const uint32_t lds0 = lds_addr_of(smem);
-  auto load_tile = [&](int u) {
-    const int hh = u / per_head;
-    const int r0 = (i0 + u % per_head) * kBQ;
+  // step u is (query head u / per_head of the group, query tile u % per_head);
+  // both are kept as running counters (no division per step): `ld_*` for the
+  // tile being loaded, `cur_*` for the tile this wave works on
+  // (load_tile is called for u = 0, 1, 2, ... in order)
+  int ld_hh = 0, ld_qi = 0, ld_slot = 0;
+  auto load_tile = [&]() {
+    const int hh = ld_hh;
+    const int r0 = (i0 + ld_qi) * kBQ;
+    const uint32_t st = lds0 + (uint32_t)ld_slot * SLOT;
+    if (++ld_qi == per_head) {
+      ld_qi = 0;
+      ++ld_hh;
+    }
+    if (++ld_slot == NSLOT) ld_slot = 0;
     const long rowbase = ((long)b * a.H + g * grp + hh) * N + r0;
     const uint32_t bytes = (uint32_t)(N - r0) * ROW;  // rows r0 .. N-1
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + rowbase * D, bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const uint16_t*)a.dout + rowbase * D, bytes);
-    const uint32_t st = lds0 + (uint32_t)(u % NSLOT) * SLOT;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) lds_dma16(rq, st + (wv + 8 * i) * 1024, toff[i]);
 #pragma unroll
@@ -357,16 +367,21 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
   // the second works on tile t-1 with the P its partner left there one step
   // earlier.  One barrier per step orders the DMA of tile t+1 (into the slot
   // tile t-2 used), the P hand-over and the reuse of the two P buffers.
-  load_tile(0);
+  load_tile();
+  int cur_qi = first ? 0 : -1;  // query tile of step u = t (first wave) or t - 1 (second)
+  int cur_slot = first ? 0 : NSLOT - 1;  // u % NSLOT
   for (int t = 0; t <= steps; ++t) {
     wait_vmem();      // this wave's pieces of tile t have landed
     __syncthreads();  // everyone's have; tile t-2's slot and P buffer are free
-    if (t + 1 < steps) load_tile(t + 1);
+    if (t + 1 < steps) load_tile();
     const int u = first ? t : t - 1;
+    const int qi = cur_qi, slot = cur_slot;
+    if (++cur_qi == per_head) cur_qi = 0;
+    if (++cur_slot == NSLOT) cur_slot = 0;
     if (u < 0 || u >= steps) continue;
-    const int r0 = (i0 + u % per_head) * kBQ;
+    const int r0 = (i0 + qi) * kBQ;
     if (CAUSAL && r0 + kBQ - 1 < kp0) continue;  // every query precedes every key of the pair
-    const unsigned char* sq = smem + (u % NSLOT) * SLOT;
+    const unsigned char* sq = smem + slot * SLOT;
     const unsigned char* sdo = sq + QT;
     const float* sl = reinterpret_cast<const float*>(sq + 2 * QT);
     const float* sd = sl + 256;

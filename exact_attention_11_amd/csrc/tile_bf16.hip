@@ -623,6 +623,8 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   const uint32_t seq_bytes = (uint32_t)(len - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, seq_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, seq_bytes);
+  // A tile past the key range (the odd half of the last step) is neither
+  // loaded nor stored: the waves of that half skip the step.
   u32x4 kr[2], vr[2];
   auto load_step = [&](int t) {
 #pragma unroll
@@ -632,19 +634,18 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
         const uint32_t off = (uint32_t)ti * (BN * row_bytes) + goff;
         kr[st] = buf_load16(rk, off);
         vr[st] = buf_load16(rv, off);
-      } else {
-        kr[st] = u32x4{0u, 0u, 0u, 0u};
-        vr[st] = kr[st];
       }
     }
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int t, int buf) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      unsigned char* sk = smem + (st * 2 + buf) * L::stage;
-      unsigned char* sv = sk + L::kBytes;
-      *reinterpret_cast<u32x4*>(sk + lrow * L::kRow + lch * 16) = kr[st];
-      *reinterpret_cast<u32x4*>(sv + lrow * L::vRow + ((lch ^ L::vswz(lrow)) << 4)) = vr[st];
+      if (2 * t + st < n_tiles) {
+        unsigned char* sk = smem + (st * 2 + buf) * L::stage;
+        unsigned char* sv = sk + L::kBytes;
+        *reinterpret_cast<u32x4*>(sk + lrow * L::kRow + lch * 16) = kr[st];
+        *reinterpret_cast<u32x4*>(sv + lrow * L::vRow + ((lch ^ L::vswz(lrow)) << 4)) = vr[st];
+      }
     }
   };
 
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
   load_step(0);
-  store_step(0);
+  store_step(0, 0);
   __syncthreads();
   for (int t = 0; t < steps; ++t) {
     const int buf = t & 1;
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (has_next) store_step(buf ^ 1);
+    if (has_next) store_step(t + 1, buf ^ 1);
     __syncthreads();
   }
 
