@@ -423,6 +423,24 @@ def test_hstu_small_every_element(d, causal):
         assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
 
 
+@pytest.mark.parametrize("B,H", [(70, 1), (1, 4), (65, 2)])
+def test_hstu_d64_unbalanced_dispatch(B, H):
+    """The d = 64 kernel deals (sequence, head) pairs to the XCDs by length
+    only for 8 <= B*H and B <= 64 (a wave ranks the sequences); more than 64
+    sequences or fewer than eight pairs take the plain pair-major mapping."""
+    _need_gpu()
+    rng = np.random.default_rng(B * 10 + H)
+    lengths = [int(v) for v in rng.integers(0, 200, B)]
+    lengths[B // 2] = 257
+    c = W.Jagged("hstu_unbalanced", B, H, 64, 1, 257, 0.3, 1.0 / 64, True, 45, 1.0)
+    x = W.jagged_inputs(c, lengths=lengths)
+    o = run_hstu(x, 1)
+    ref = hstu_ref(x, True)
+    for b, r in ref.items():
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
+
+
 def test_hstu_d128_multi_round():
     """d = 128 jagged HSTU whose grid is too large to pair (16 sequences x 4
     heads x 16 slots > 768 resident workgroups): one query block per
