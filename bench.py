@@ -222,13 +222,15 @@ def counters_report(dirs, kernel_substr: str, trace_dir=None) -> None:
     mfma = vals.get("SQ_INSTS_MFMA", float("nan"))
     if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
         print(f"mfma_busy_fraction           {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.3f}")
-        print(f"mfma_busy_cycles_per_mfma    {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.1f}")
-    for ctr, label in (("SQ_INSTS_VALU", "valu_non_mfma_per_mfma"), ("SQ_INSTS_SALU", "salu_per_mfma"),
-                       ("SQ_INSTS_LDS", "lds_per_mfma"), ("SQ_INSTS_VMEM", "vmem_per_mfma"),
-                       ("SQ_INSTS_VALU_TRANS_F32", "trans_per_mfma")):
-        if ctr in vals:
-            v = vals[ctr] - (mfma if ctr == "SQ_INSTS_VALU" else 0)
-            print(f"{label:28s} {v / mfma:.2f}")
+        if mfma > 0:
+            print(f"mfma_busy_cycles_per_mfma    {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / mfma:.1f}")
+    if mfma > 0:  # instruction mix per matrix product (kernels without products: the counts above)
+        for ctr, label in (("SQ_INSTS_VALU", "valu_non_mfma_per_mfma"), ("SQ_INSTS_SALU", "salu_per_mfma"),
+                           ("SQ_INSTS_LDS", "lds_per_mfma"), ("SQ_INSTS_VMEM", "vmem_per_mfma"),
+                           ("SQ_INSTS_VALU_TRANS_F32", "trans_per_mfma")):
+            if ctr in vals:
+                v = vals[ctr] - (mfma if ctr == "SQ_INSTS_VALU" else 0)
+                print(f"{label:28s} {v / mfma:.2f}")
     if "SQ_BUSY_CYCLES" in vals:
         # SQ_BUSY_CYCLES is summed over the 32 shader engines
         print(f"sq_busy_fraction             {vals['SQ_BUSY_CYCLES'] / 32 / gui:.3f}   (SQ_BUSY_CYCLES / 32 SEs)")
@@ -240,7 +242,10 @@ def counters_report(dirs, kernel_substr: str, trace_dir=None) -> None:
                         if kernel_substr in r.get("Kernel_Name", ""))
             if ds:
                 print(f"dispatch_us                  {' '.join(f'{x / 1e3:.1f}' for x in ds)}   (kernel-trace run)")
-                print(f"gpu_clock_ghz                {gui / ds[0]:.2f}   (GRBM_GUI_ACTIVE per XCD / fastest dispatch)")
+                if ds[0] >= 50_000:
+                    print(f"gpu_clock_ghz                {gui / ds[0]:.2f}   (GRBM_GUI_ACTIVE per XCD / fastest dispatch)")
+                else:  # the active count also covers the launch's start and drain
+                    print("gpu_clock_ghz                n/a   (dispatch under 50 us)")
 
 
 PREFILL_KERNEL = "tile_kernel<128, true, (fattn::Epilogue)0, false>"
@@ -629,8 +634,13 @@ def main(argv=None) -> int:
         out["decode"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "ms_per_call": round(ms["decode"], 4), "median_ms_per_call": round(med["decode"], 4),
                          "algorithmic_bytes": nbytes, "sum_L": ssum, "splits": args.splits or "auto"}
+        if out["value"] is None:
+            out.update({"value": round(gbs, 1), "unit": "GB/s"})
+    if "decode" in parts and not args.only:
         # the same decode at 16, 32 and 64 chunks per sequence (the automatic
-        # count above is 768 work items in all, 6 chunks per sequence here)
+        # count above is 768 work items in all, 6 chunks per sequence here);
+        # left out of single-part runs, whose counter profiles then cover the
+        # automatic split alone
         sweep = {}
         swsb = fa.attn_decode_workspace_bytes(dc.B, dc.H, dc.d, 64)
         sws = torch.empty(swsb // 4, dtype=torch.float32, device=dev)
@@ -642,8 +652,6 @@ def main(argv=None) -> int:
                               "ms_per_call": round(ms_s, 4)}
         out["decode"]["splits_sweep"] = sweep
         del sws
-        if out["value"] is None:
-            out.update({"value": round(gbs, 1), "unit": "GB/s"})
     if "decode_paged" in parts:
         ssum = int(dx.seqlens.sum())
         # same algorithmic bytes as the contiguous decode (the block-table reads,
