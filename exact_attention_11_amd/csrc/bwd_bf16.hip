@@ -434,14 +434,18 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
         for (int j = 0; j < 4; ++j)
           lv[j] = *reinterpret_cast<const f32x4*>(sl + 32 * mb + 16 * (j >> 1) + 8 * g2 + 4 * (j & 1));
         float p[16];
+        // the mask test stays outside the element loop: one uniform branch per
+        // block, selects inside it
+        if (masked) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = s[mb][e];
-          if (masked) {
+          for (int e = 0; e < 16; ++e) {
             const int row = r0 + 32 * mb + acc_key(e, g2);
-            if (!(row < N && (!CAUSAL || key <= row))) x = kNegInf;
+            const float x = (row < N && (!CAUSAL || key <= row)) ? s[mb][e] : kNegInf;
+            p[e] = exp2_hw(__builtin_fmaf(x, c2, -lv[e >> 2][e & 3] * kLog2e));
           }
-          p[e] = exp2_hw(__builtin_fmaf(x, c2, -lv[e >> 2][e & 3] * kLog2e));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = exp2_hw(__builtin_fmaf(s[mb][e], c2, -lv[e >> 2][e & 3] * kLog2e));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[mb][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
