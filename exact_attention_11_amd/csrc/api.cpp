@@ -347,10 +347,16 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   return hip_status(fattn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_paged launch");
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int N) {
-  if (B < 0 || H < 1 || N < 0) return 0;
+// two f32 arrays over the query rows, each rounded up to 256 bytes: the row
+// sums delta, then -LSE log2(e)
+static size_t bwd_row_array_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) / 256 * 256;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 0 || H < 1 || N < 0) return 0;
+  return 2 * bwd_row_array_bytes(B, H, N);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -382,6 +388,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.nlse = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bwd_row_array_bytes(B, H, N));
   a.B = B;
   a.H = H;
   a.Hkv = Hkv;

@@ -15,7 +15,8 @@
 //    (32x32x16 products, keys on the M side), dS^T in registers, then
 //    dQ^T += K^T dS^T with K^T gathered by transposing LDS reads.  It also
 //    computes delta for its rows (from dO and O, already in registers for the
-//    fragment loads) and stores it for the second kernel.
+//    fragment loads) and stores it, with -LSE log2(e) of each row, for the
+//    second kernel.
 //  * bwd_dkdv_kernel, one workgroup of 8 waves per 128 keys of a (batch,
 //    kv-head): four wave pairs of 32 keys each, the keys being the columns of
 //    32x32x16 products.  Per tile of 64 query rows (of every query head of
@@ -131,9 +132,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
   }
   const float delta = dsum + xor32(dsum);
   const long rowidx = ((long)b * a.H + h) * N + qrow;
-  if (row_ok && g2 == 0) a.delta[rowidx] = delta;
   // -LSE in base 2; rows past the end get -inf, so their weights are 0
   const float nl = row_ok ? -a.lse[rowidx] * kLog2e : kNegInf;
+  // both row values go to the workspace for the dK/dV kernel
+  if (row_ok && g2 == 0) {
+    a.delta[rowidx] = delta;
+    a.nlse[rowidx] = nl;
+  }
   const float c2 = a.c;
 
   // K/V tile loads: wave instruction i fills LDS bytes (wv + 4i) KB .. +1 KB
@@ -260,7 +265,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
   constexpr int ROW = D * 2;
   constexpr int QT = kBQ * ROW;        // bytes of a Q or dO tile
-  constexpr int SLOT = 2 * QT + 2048;  // Q, dO, LSE (1 KB), delta (1 KB)
+  constexpr int SLOT = 2 * QT + 2048;  // Q, dO, -LSE log2(e) (1 KB), delta (1 KB)
   constexpr int NSLOT = 3;             // tiles u-1 (second waves), u (first waves), u+1 (loading)
   constexpr int PBUF = kBQ * 32 * 2;   // P of one pair and tile, bf16
   constexpr int NLD = QT / 1024 / 8;   // 1 KB direct loads per wave, tensor and tile
@@ -350,9 +355,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
     for (int i = 0; i < NLD; ++i) lds_dma16(rq, st + (wv + 8 * i) * 1024, toff[i]);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) lds_dma16(rd, st + QT + (wv + 8 * i) * 1024, toff[i]);
-    // LSE and delta of rows r0 .. r0+63 (1 KB of LDS each; lanes past the 64
-    // values land in the unused rest of the region)
-    if (wv == 0) lds_dma16(make_rsrc(a.lse + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT, 16u * lane);
+    // -LSE log2(e) and delta of rows r0 .. r0+63, both from the dQ kernel (1 KB
+    // of LDS each; lanes past the 64 values land in the unused rest of the
+    // region)
+    if (wv == 0) lds_dma16(make_rsrc(a.nlse + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT, 16u * lane);
     if (wv == 1) lds_dma16(make_rsrc(a.delta + rowbase, (uint32_t)(N - r0) * 4), st + 2 * QT + 1024, 16u * lane);
   };
 
@@ -441,11 +447,11 @@ __global__ __launch_bounds__(kPairThreads, 2) void bwd_dkdv_kernel(BwdArgs a, in
           for (int e = 0; e < 16; ++e) {
             const int row = r0 + 32 * mb + acc_key(e, g2);
             const float x = (row < N && (!CAUSAL || key <= row)) ? s[mb][e] : kNegInf;
-            p[e] = exp2_hw(__builtin_fmaf(x, c2, -lv[e >> 2][e & 3] * kLog2e));
+            p[e] = exp2_hw(__builtin_fmaf(x, c2, lv[e >> 2][e & 3]));
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) p[e] = exp2_hw(__builtin_fmaf(s[mb][e], c2, -lv[e >> 2][e & 3] * kLog2e));
+          for (int e = 0; e < 16; ++e) p[e] = exp2_hw(__builtin_fmaf(s[mb][e], c2, lv[e >> 2][e & 3]));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[mb][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);

@@ -110,6 +110,7 @@ struct BwdArgs {
   void* dk;           // [B, Hkv, N, d] bf16
   void* dv;
   float* delta;       // workspace [B, H, N]: rowsum(dO * O)
+  float* nlse;        // workspace [B, H, N]: -LSE log2(e), the base-2 offset of P's exponent
   int B, H, Hkv, N, d;
   float scale;        // softmax scale
   float c;            // scale * log2(e), clamped to >= FLT_MIN

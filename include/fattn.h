@@ -233,9 +233,10 @@ int attn_hstu_jagged(const void* q, const void* k, const void* v, void* o,
                      float alpha, float inv_n, int causal, void* stream);
 
 /*
- * attn_bwd_workspace_bytes -- device workspace attn_bwd needs: one f32 per
- * query row (the row sums delta below), rounded up to 256 bytes.  Returns 0
- * for an invalid shape.
+ * attn_bwd_workspace_bytes -- device workspace attn_bwd needs: two f32 arrays
+ * over the B*H*N query rows, each rounded up to 256 bytes (the row sums
+ * delta below, and each row's -LSE log2(e), which the key-block kernel reads
+ * instead of scaling the LSE itself).  Returns 0 for an invalid shape.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
@@ -260,7 +261,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
  *   dq           bf16 [B, H,   N, d]  written
  *   dk, dv       bf16 [B, Hkv, N, d]  written
  *   workspace    device buffer of at least attn_bwd_workspace_bytes(B, H, N)
- *                bytes; contents on entry are ignored (it receives delta).
+ *                bytes; contents on entry are ignored (it receives delta and
+ *                -LSE log2(e) per row).
  *   H % Hkv == 0; d in {64, 128}; scale finite and >= 0; causal in {0, 1}.
  *   B == 0 or N == 0 is a valid empty call.
  */

@@ -229,9 +229,9 @@ def test_attn_bwd_rejects(kw, status):
 
 
 def test_bwd_workspace_size_and_empty_calls():
-    # one f32 per query row, rounded to 256 B
-    assert fa.attn_bwd_workspace_bytes(2, 4, 100) == 3328
-    assert fa.attn_bwd_workspace_bytes(8, 32, 4096) == 8 * 32 * 4096 * 4
+    # two f32 arrays over the query rows (delta, -LSE log2 e), each rounded to 256 B
+    assert fa.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 3328
+    assert fa.attn_bwd_workspace_bytes(8, 32, 4096) == 2 * 8 * 32 * 4096 * 4
     assert fa.attn_bwd_workspace_bytes(1, 0, 10) == 0
     _bwd(q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, workspace=0, B=0)
     _bwd(q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, workspace=0, N=0)
