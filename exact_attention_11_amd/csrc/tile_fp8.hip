@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
