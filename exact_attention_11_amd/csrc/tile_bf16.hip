@@ -21,9 +21,11 @@
 // one d column.  V rows are XOR-swizzled in 16-byte chunks so that the four key
 // rows one read touches fall in different banks.
 //
-// K and V tiles are fetched with buffer loads whose descriptor covers only the
-// valid rows of the sequence: rows past the end read as zero, so no load is
-// predicated.
+// K and V tiles go straight from HBM into LDS (buffer_load ... lds: no
+// staging registers, no LDS store instructions in the wave), the next tile's
+// loads issued into the free buffer as a tile starts and waited for at its
+// barrier.  The load descriptor covers only the valid rows of the sequence:
+// rows past the end read as zero, so no load is predicated.
 //
 // Two pointwise epilogues share the loop:
 //  * Softmax: online softmax with a running row max m and running sum l
@@ -57,7 +59,7 @@ constexpr int kBM = 128;              // query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 // Keys per K/V tile.  Smaller tiles leave room for more waves per SIMD: with
-// 32-key tiles the d = 128 kernel needs at most 168 registers and 33 KB of LDS,
+// 32-key tiles the d = 128 kernel needs at most 168 registers and 32 KB of LDS,
 // so three workgroups (12 waves) share a CU; the d = 64 kernel fits four
 // (at most 128 registers, 34 KB).  Every wave's step is a serial chain
 // (products, softmax, products); more waves per SIMD keep the matrix cores fed
@@ -105,6 +107,25 @@ struct Cfg<64> {
   static constexpr int kVAhead = 0;
 };
 
+// Layout of one K/V stage filled by direct HBM->LDS loads (1 KB of
+// consecutive LDS bytes per wave instruction, so no row padding): K rows of
+// D bf16 with 16-byte chunks XOR-swizzled by kswz, V rows as in Lds.
+template <int D, int BN>
+struct LdsDma {
+  static constexpr int kRow = D * 2;
+  static constexpr int kBytes = BN * kRow;
+  static constexpr int vRow = D * 2;
+  static constexpr int vBytes = BN * vRow;
+  static constexpr int stage = kBytes + vBytes;
+  static constexpr int total = 2 * stage;
+  // 16 lanes of a K fragment read (16 distinct rows, one chunk column) hit 16
+  // distinct 16-byte bank groups
+  __device__ static __forceinline__ int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+  __device__ static __forceinline__ int vswz(int r) { return D >= 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
+};
+
+// Layout of one K/V stage written by the waves' own LDS stores (the d = 64
+// HSTU kernel): K rows padded by 16 bytes, V rows swizzled.
 template <int D, int BN>
 struct Lds {
   static constexpr int kRow = (D + 8) * 2;  // K row: D bf16 + 16-byte pad
@@ -144,7 +165,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-row blocks of d
   constexpr int NDC = D / 16;   // K=16 steps over d
-  using L = Lds<D, BN>;
+  using L = LdsDma<D, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x;
@@ -221,40 +242,32 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
       qf[c] = as_bf16x8(t);
     }
 
-    // ---- global -> register staging of one K/V tile (buffer loads; rows past
-    // the sequence end read as zero)
-    constexpr int KCH = D / 8;                   // 16-byte chunks per row
-    constexpr int NLD = BN * KCH / kThreads;     // 16-byte loads per thread per tensor
+    // ---- direct HBM -> LDS loads of one K/V tile: wave instruction i fills
+    // bytes (wv + 4i) KB .. +1 KB of each tensor's tile; the chunk swizzles are
+    // applied through the source address (rows past the sequence end read as
+    // zero)
+    constexpr int NLW = BN * D * 2 / 1024 / 4;  // 1 KB loads per wave and tensor
+    static_assert(NLW * 4 * 1024 == BN * D * 2, "tile split over four waves");
     const uint32_t row_bytes = (uint32_t)row_stride * 2;
-    uint32_t goff[NLD];  // byte offset of this thread's chunks within a tile
-    int lds_row[NLD], lds_chunk[NLD];
+    uint32_t koff[NLW], voff[NLW];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int ci = tid + kThreads * i;
-      lds_row[i] = ci / KCH;
-      lds_chunk[i] = ci % KCH;
-      goff[i] = (uint32_t)lds_row[i] * row_bytes + (uint32_t)lds_chunk[i] * 16u;
+    for (int i = 0; i < NLW; ++i) {
+      const int byte = (wv + 4 * i) * 1024 + 16 * lane;
+      const int r = byte / (D * 2);
+      const int pc = (byte % (D * 2)) / 16;
+      koff[i] = (uint32_t)r * row_bytes + (uint32_t)(pc ^ L::kswz(r)) * 16u;
+      voff[i] = (uint32_t)r * row_bytes + (uint32_t)(pc ^ L::vswz(r)) * 16u;
     }
-    u32x4 kr[NLD], vr[NLD];
-
-    auto load_tile = [&](int k0) {
-      // valid bytes from row k0: rows k0 .. len-1 of this head
+    const uint32_t lds0 = lds_addr_of(smem);
+    auto dma_tile = [&](int k0, int buf) {
       const uint32_t bytes = (uint32_t)(len - k0 - 1) * row_bytes + D * 2;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * row_stride, bytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * row_stride, bytes);
+      const uint32_t st = lds0 + (uint32_t)buf * L::stage;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) kr[i] = buf_load16(rk, goff[i]);
+      for (int i = 0; i < NLW; ++i) lds_dma16(rk, st + (wv + 4 * i) * 1024, koff[i]);
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) vr[i] = buf_load16(rv, goff[i]);
-    };
-    auto store_tile = [&](int buf) {
-      unsigned char* sk = smem + buf * L::stage;
-      unsigned char* sv = sk + L::kBytes;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        *reinterpret_cast<u32x4*>(sk + lds_row[i] * L::kRow + lds_chunk[i] * 16) = kr[i];
-        *reinterpret_cast<u32x4*>(sv + lds_row[i] * L::vRow + ((lds_chunk[i] ^ L::vswz(lds_row[i])) << 4)) = vr[i];
-      }
+      for (int i = 0; i < NLW; ++i) lds_dma16(rv, st + L::kBytes + (wv + 4 * i) * 1024, voff[i]);
     };
 
     // per-lane part of the transposing V^T reads: row offset within the 8-key
@@ -273,15 +286,16 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
     float l_part = 0.f;     // this lane's share of the row sum
     const float cexp = a.c;
 
-    load_tile(0);
-    store_tile(0);
+    dma_tile(0, 0);
+    wait_vmem();
     __syncthreads();
 
     for (int j = 0; j < n_tiles; ++j) {
       const int buf = j & 1;
       const int k0 = j * BN;
       const bool has_next = j + 1 < n_tiles;
-      if (has_next) load_tile(k0 + BN);
+      // the other buffer's tile was last read before the previous barrier
+      if (has_next) dma_tile(k0 + BN, buf ^ 1);
 
       const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
       if (active) {
@@ -291,7 +305,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
         // S^T = K Q^T
         f32x16 s[NKB];
         auto kread = [&](int c, int kb) {
-          return *reinterpret_cast<const u32x4*>(sk + (32 * kb + key_perm(n32)) * L::kRow + (16 * c + 8 * g2) * 2);
+          const int kr_ = 32 * kb + key_perm(n32);
+          return *reinterpret_cast<const u32x4*>(sk + kr_ * L::kRow + (((2 * c + g2) ^ L::kswz(kr_)) << 4));
         };
         if constexpr (Cfg<D>::kKAhead == 0) {
 #pragma unroll
@@ -444,8 +459,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
       }
 
       __builtin_amdgcn_s_setprio(0);
-      if (has_next) store_tile(buf ^ 1);
-      __syncthreads();
+      wait_vmem();      // this wave's pieces of the next tile have landed
+      __syncthreads();  // everyone's have; this tile's buffer is free
     }
 
     if (!wave_live || qrow >= len) return;

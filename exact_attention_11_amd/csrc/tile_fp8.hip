@@ -16,8 +16,8 @@
 // mask with tile skipping); descale_q * descale_k folds into the exponent's
 // FMA and descale_v into the final 1/l.  One workgroup of four waves owns 128
 // query rows of one (batch, head), 32 per wave; K and V tiles of 64 keys are
-// staged through double-buffered LDS (register-staged buffer loads, rows past
-// the sequence end read as zero).  At most 168 registers per lane, so three
+// staged through double-buffered LDS by direct HBM->LDS buffer loads (rows
+// past the sequence end read as zero).  At most 168 registers per lane, so three
 // workgroups (12 waves) share a CU.
 //
 // Lane layouts of the 32x32x64 FP8 product (A, B: lane l holds row / column
@@ -117,37 +117,30 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
     qf[c] = cat(lo, hi);
   }
 
-  // tile staging: thread chunk ci = tid + 256 i is LDS row ci / KCH, chunk ci % KCH;
-  // K rows are fetched in kidx order, V rows in natural order
-  uint32_t kgo[NLD], vgo[NLD], klo[NLD], vlo[NLD];
+  // direct HBM -> LDS tile loads: wave instruction i fills bytes (wv + 4i) KB
+  // .. +1 KB of each tensor's tile.  LDS row r of K holds key kidx(r), of V
+  // key r; the chunk swizzles are applied through the source address (rows
+  // past the sequence end read as zero)
+  constexpr int NLW = TILE / 1024 / 4;  // 1 KB loads per wave and tensor
+  static_assert(NLW * 4 * 1024 == TILE, "tile split over four waves");
+  uint32_t kgo[NLW], vgo[NLW];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int ci = tid + kThreads * i;
-    const int r = ci / KCH, ch = ci % KCH;
-    kgo[i] = (uint32_t)kidx(r) * ROW + ch * 16;
-    vgo[i] = (uint32_t)r * ROW + ch * 16;
-    klo[i] = (uint32_t)r * ROW + ((ch ^ swz_k(r)) << 4);
-    vlo[i] = (uint32_t)r * ROW + ((ch ^ swz_v(r)) << 4);
+  for (int i = 0; i < NLW; ++i) {
+    const int byte = (wv + 4 * i) * 1024 + 16 * lane;
+    const int r = byte / ROW, pc = (byte % ROW) / 16;
+    kgo[i] = (uint32_t)kidx(r) * ROW + (uint32_t)((pc ^ swz_k(r)) << 4);
+    vgo[i] = (uint32_t)r * ROW + (uint32_t)((pc ^ swz_v(r)) << 4);
   }
-  u32x4 kr[NLD], vr[NLD];
-  auto load_tile = [&](int k0) {
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto dma_tile = [&](int k0, int buf) {
     const uint32_t bytes = (uint32_t)(N - k0) * ROW;  // rows k0 .. N-1
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (long)k0 * ROW, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (long)k0 * ROW, bytes);
+    const uint32_t st = lds0 + (uint32_t)buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kr[i] = buf_load16(rk, kgo[i]);
-      vr[i] = buf_load16(rv, vgo[i]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* sk = smem + buf * STAGE;
-    unsigned char* sv = sk + TILE;
+    for (int i = 0; i < NLW; ++i) lds_dma16(rk, st + (wv + 4 * i) * 1024, kgo[i]);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      *reinterpret_cast<u32x4*>(sk + klo[i]) = kr[i];
-      *reinterpret_cast<u32x4*>(sv + vlo[i]) = vr[i];
-    }
+    for (int i = 0; i < NLW; ++i) lds_dma16(rv, st + TILE + (wv + 4 * i) * 1024, vgo[i]);
   };
 
   // 8-bit transposing reads of V^T: within 16-lane group g4, lane j addresses
@@ -165,15 +158,16 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
   float m_ref = kNegInf;
   float l_part = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  dma_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int k0 = j * kBN;
     const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(k0 + kBN);
+    // the other buffer's tile was last read before the previous barrier
+    if (has_next) dma_tile(k0 + kBN, buf ^ 1);
 
     const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
     if (active) {
@@ -262,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
     }
 
     __builtin_amdgcn_s_setprio(0);
-    if (has_next) store_tile(buf ^ 1);
+    wait_vmem();  // this wave's pieces of the next tile have landed
     __syncthreads();
   }
 
