@@ -108,10 +108,10 @@ struct Cfg<64> {
 };
 
 // Layout of one K/V stage filled by direct HBM->LDS loads (1 KB of
-// consecutive LDS bytes per wave instruction, so no row padding): K rows of
-// D bf16 with 16-byte chunks XOR-swizzled by kswz, V rows as in Lds.
+// consecutive LDS bytes per wave instruction, so no row padding): rows of D
+// bf16 whose 16-byte chunks are XOR-swizzled, by kswz for K and vswz for V.
 template <int D, int BN>
-struct LdsDma {
+struct Lds {
   static constexpr int kRow = D * 2;
   static constexpr int kBytes = BN * kRow;
   static constexpr int vRow = D * 2;
@@ -121,22 +121,8 @@ struct LdsDma {
   // 16 lanes of a K fragment read (16 distinct rows, one chunk column) hit 16
   // distinct 16-byte bank groups
   __device__ static __forceinline__ int kswz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
-  __device__ static __forceinline__ int vswz(int r) { return D >= 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
-};
-
-// Layout of one K/V stage written by the waves' own LDS stores (the d = 64
-// HSTU kernel): K rows padded by 16 bytes, V rows swizzled.
-template <int D, int BN>
-struct Lds {
-  static constexpr int kRow = (D + 8) * 2;  // K row: D bf16 + 16-byte pad
-  static constexpr int kBytes = BN * kRow;
-  static constexpr int vRow = D * 2;        // V row: D bf16, 16-byte chunks swizzled
-  static constexpr int vBytes = BN * vRow;
-  static constexpr int stage = kBytes + vBytes;
-  static constexpr int total = 2 * stage;
-  // XOR applied to the 16-byte chunk index of V row r: the 4 consecutive rows a
-  // transposing read touches land on disjoint banks (bits >= 2 of the chunk
-  // index only, so 32-byte pieces stay contiguous).
+  // the 4 consecutive rows a transposing read touches land on disjoint banks
+  // (bits >= 2 of the chunk index only, so 32-byte pieces stay contiguous)
   __device__ static __forceinline__ int vswz(int r) { return D >= 128 ? ((r & 3) << 2) : ((r & 2) << 1); }
 };
 
@@ -165,7 +151,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-row blocks of d
   constexpr int NDC = D / 16;   // K=16 steps over d
-  using L = LdsDma<D, BN>;
+  using L = Lds<D, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
 
   const int tid = threadIdx.x;
@@ -628,38 +614,35 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
     qf[c] = as_bf16x8(t);
   }
 
-  // step t loads tiles 2t and 2t+1: one 16-byte chunk of K and of V per
-  // thread and tile
+  // step t loads tiles 2t and 2t+1 straight into LDS: wave instruction w
+  // fills bytes w KB .. +1 KB of each tensor's tile (the chunk swizzles applied
+  // through the source address)
   const uint32_t row_bytes = (uint32_t)rs * 2;
-  const int lrow = tid >> 3, lch = tid & 7;
-  const uint32_t goff = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16u;
+  static_assert(BN * D * 2 == 4 * 1024, "one 1 KB load per wave, tile and tensor");
+  uint32_t koff, voff;
+  {
+    const int byte = wv * 1024 + 16 * lane;
+    const int r = byte / (D * 2), pc = (byte % (D * 2)) / 16;
+    koff = (uint32_t)r * row_bytes + (uint32_t)((pc ^ L::kswz(r)) << 4);
+    voff = (uint32_t)r * row_bytes + (uint32_t)((pc ^ L::vswz(r)) << 4);
+  }
   // one descriptor per tensor over rows [0, len) of this head: rows past the
   // sequence end read as zero
   const uint32_t seq_bytes = (uint32_t)(len - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, seq_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, seq_bytes);
-  // A tile past the key range (the odd half of the last step) is neither
-  // loaded nor stored: the waves of that half skip the step.
-  u32x4 kr[2], vr[2];
-  auto load_step = [&](int t) {
+  const uint32_t lds0 = lds_addr_of(smem);
+  // A tile past the key range (the odd half of the last step) is not loaded:
+  // the waves of that half skip the step.
+  auto dma_step = [&](int t, int buf) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int ti = 2 * t + st;
       if (ti < n_tiles) {
-        const uint32_t off = (uint32_t)ti * (BN * row_bytes) + goff;
-        kr[st] = buf_load16(rk, off);
-        vr[st] = buf_load16(rv, off);
-      }
-    }
-  };
-  auto store_step = [&](int t, int buf) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (2 * t + st < n_tiles) {
-        unsigned char* sk = smem + (st * 2 + buf) * L::stage;
-        unsigned char* sv = sk + L::kBytes;
-        *reinterpret_cast<u32x4*>(sk + lrow * L::kRow + lch * 16) = kr[st];
-        *reinterpret_cast<u32x4*>(sv + lrow * L::vRow + ((lch ^ L::vswz(lrow)) << 4)) = vr[st];
+        const uint32_t off = (uint32_t)ti * (BN * row_bytes);
+        const uint32_t sk = lds0 + (uint32_t)(st * 2 + buf) * L::stage;
+        lds_dma16(rk, sk + wv * 1024, off + koff);
+        lds_dma16(rv, sk + L::kBytes + wv * 1024, off + voff);
       }
     }
   };
@@ -674,13 +657,14 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
-  load_step(0);
-  store_step(0, 0);
+  dma_step(0, 0);
+  wait_vmem();
   __syncthreads();
   for (int t = 0; t < steps; ++t) {
     const int buf = t & 1;
     const bool has_next = t + 1 < steps;
-    if (has_next) load_step(t + 1);
+    // the other buffers' tiles were last read before the previous barrier
+    if (has_next) dma_step(t + 1, buf ^ 1);
     const int ti = 2 * t + ks;
     const int k0 = ti * BN;
     const bool active = wave_live && ti < n_tiles && !(CAUSAL && k0 > q0w + 31);
@@ -691,7 +675,8 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
       f32x16 s;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + key_perm(n32) * L::kRow + (16 * c + 8 * g2) * 2);
+        const int kr_ = key_perm(n32);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + kr_ * L::kRow + (((2 * c + g2) ^ L::kswz(kr_)) << 4));
         const f32x16 zero = {};
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s, 0, 0, 0);
       }
@@ -728,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (has_next) store_step(t + 1, buf ^ 1);
+    wait_vmem();  // this wave's pieces of the next step's tiles have landed
     __syncthreads();
   }
 
