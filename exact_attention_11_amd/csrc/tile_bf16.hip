@@ -61,7 +61,7 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 // Keys per K/V tile.  Smaller tiles leave room for more waves per SIMD: with
 // 32-key tiles the d = 128 kernel needs at most 168 registers and 32 KB of LDS,
 // so three workgroups (12 waves) share a CU; the d = 64 kernel fits four
-// (at most 128 registers, 34 KB).  Every wave's step is a serial chain
+// (at most 128 registers, 32 KB).  Every wave's step is a serial chain
 // (products, softmax, products); more waves per SIMD keep the matrix cores fed
 // while some of them are in the softmax.
 template <int D>
