@@ -399,7 +399,8 @@ def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, 
                                 "TFLOP/s": round(f / (ms_nc * 1e-3) / 1e12, 2),
                                 "frac_bf16_peak": round(f / (ms_nc * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     for key, c, label in (("prefill_long", W.PREFILL_LONG, "B=1 H=32 N=32768 d=128 bf16 causal"),
-                          ("prefill_d64", W.PREFILL_D64, "B=1 H=32 N=4096 d=64 bf16 causal")):
+                          ("prefill_d64", W.PREFILL_D64, "B=1 H=32 N=4096 d=64 bf16 causal"),
+                          ("prefill_d256", W.PREFILL_D256, "B=4 H=32 N=4096 d=256 bf16 causal")):
         x = W.dense_inputs(c)
         cq, ck, cv = bf16(x.q), bf16(x.k), bf16(x.v)
         del x

@@ -12,6 +12,8 @@ The five workloads (sizes from the pages' examples where they give them):
   and non-causal -- the batch 8 / seq 4096 / head_dim 128 setting of the CANN
   ops-transformer page's measurement table.
 * ``prefill_long``  B=1, H=32, N=32768, d=128, bf16, causal.
+* ``prefill_d256``  B=4, H=32, N=4096, d=256, bf16, scale 1/16, causal (the
+  widest head dimension the forward kernel takes).
 * ``decode_gqa``    B=16, H=32, Hkv=8, Lmax=32768, lengths uniform on
   [16384, 32768], d=128, bf16, scale 1/sqrt(128).  Cache rows at or beyond a
   sequence's length hold NaN so that reading them would show.
@@ -21,7 +23,9 @@ The five workloads (sizes from the pages' examples where they give them):
   three.
 
 Seeds: workload k of the list above (tiny=0 ... hstu=4) uses seed 1000+k;
-``prefill_long`` shares seed 1002 with ``prefill_d128``.
+``prefill_long`` shares seed 1002 with ``prefill_d128``; ``prefill_d256``
+uses seed 1003 (as the decode workload: a different shape, so different
+draws).
 """
 
 from __future__ import annotations
@@ -97,6 +101,7 @@ PREFILL_D64 = Dense("prefill_d64", 1, 32, 32, 4096, 64, 1.0 / 8.0, True, "bf16",
 PREFILL_D128_CAUSAL = Dense("prefill_d128_causal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), True, "bf16", 1002)
 PREFILL_D128_FULL = Dense("prefill_d128_noncausal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), False, "bf16", 1002)
 PREFILL_LONG = Dense("prefill_long", 1, 32, 32, 32768, 128, 1.0 / math.sqrt(128.0), True, "bf16", 1002)
+PREFILL_D256 = Dense("prefill_d256", 4, 32, 32, 4096, 256, 1.0 / 16.0, True, "bf16", 1003)
 PREFILL_FP8 = Dense("prefill_fp8_d128_causal", 8, 32, 32, 4096, 128, 1.0 / math.sqrt(128.0), True, "fp8", 1006)
 DECODE_GQA = Decode("decode_gqa", 16, 32, 8, 32768, 128, 1.0 / math.sqrt(128.0), 16384, 32768, 1003)
 HSTU_JAGGED = Jagged("hstu_jagged", 16, 4, 64, 512, 4096, 1.0 / 8.0, 1.0 / 4096.0, True, 1004)
