@@ -41,7 +41,7 @@ def _prefill_case(i):
     return dict(B=B, H=G * Hkv, Hkv=Hkv, N=N, d=d, causal=causal, scale=scale, seed=7100 + i)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(96))
 def test_random_prefill(i):
     _need_gpu()
     c = _prefill_case(i)
@@ -75,7 +75,7 @@ def _decode_case(i):
                 seed=7200 + i)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_decode_contiguous_and_paged(i):
     _need_gpu()
     c = _decode_case(i)
@@ -135,7 +135,7 @@ def _hstu_case(i):
     return dict(B=B, H=H, d=d, lens=lens, causal=causal, alpha=alpha, seed=7300 + i)
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_random_hstu(i):
     _need_gpu()
     c = _hstu_case(i)
@@ -172,7 +172,7 @@ def _bwd_case(i):
     return dict(B=B, H=G * Hkv, Hkv=Hkv, N=N, d=d, causal=causal, scale=scale, seed=7400 + i)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(32))
 def test_random_backward(i):
     _need_gpu()
     from synthgen import TENSOR_DO
@@ -211,7 +211,7 @@ def _fp8_case(i):
     return dict(B=B, H=G * Hkv, Hkv=Hkv, N=N, causal=causal, seed=7500 + i)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(32))
 def test_random_fp8(i):
     _need_gpu()
     from _util import assert_fp8
