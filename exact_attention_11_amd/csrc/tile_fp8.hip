@@ -176,19 +176,34 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
       __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with softmax work
       // S^T = K Q^T: 32-key block kb = LDS rows 32 kb .. +32
       f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      // step t = (c, kb) with kb minor: consecutive products are independent;
+      // each K fragment read KW products ahead, the order pinned (reads, then
+      // one product and one fragment at a time)
+      constexpr int ST = 2 * NKC;
+      constexpr int KW = 2;
+      u32x4 klo[ST], khi[ST];
+      auto kread = [&](int t) {
+        const int kb = t % 2, c = t / 2;
         const int r = 32 * kb + n32;
-        f32x16 t = {};
+        const int ch = 4 * c + 2 * g2;
+        klo[t] = *reinterpret_cast<const u32x4*>(sk + r * ROW + ((ch ^ swz_k(r)) << 4));
+        khi[t] = *reinterpret_cast<const u32x4*>(sk + r * ROW + (((ch + 1) ^ swz_k(r)) << 4));
+      };
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) {
-          const int ch = 4 * c + 2 * g2;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(sk + r * ROW + ((ch ^ swz_k(r)) << 4));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(sk + r * ROW + (((ch + 1) ^ swz_k(r)) << 4));
-          t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(lo, hi), qf[c], t, 0, 0, 0, kUnitScale, 0,
-                                                              kUnitScale);
-        }
-        s[kb] = t;
+      for (int t = 0; t < KW; ++t) kread(t);
+#pragma unroll
+      for (int t = 0; t < ST; ++t) {
+        const int kb = t % 2, c = t / 2;
+        const f32x16 zero = {};
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(klo[t], khi[t]), qf[c], c == 0 ? zero : s[kb], 0,
+                                                                0, 0, kUnitScale, 0, kUnitScale);
+        if (t + KW < ST) kread(t + KW);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KW, 0);
+#pragma unroll
+      for (int t = 0; t < ST; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t + KW < ST) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
 
       __builtin_amdgcn_s_setprio(0);
