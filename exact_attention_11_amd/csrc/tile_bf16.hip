@@ -520,15 +520,22 @@ hipError_t launch_causal(const TileArgs& a, hipStream_t s) {
 // snake order -- ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs 7..0, and so
 // on -- so every XCD gets a near-equal share of the quadratic work while all
 // query blocks of a pair stay on one XCD (its K and V in that XCD's L2).  Each
-// XCD dispatches the query blocks of all its pairs heaviest first: rank u
-// within the XCD is block nqb - 1 - u / n_x of its pair u % n_x.  One lane per
-// sequence ranks the lengths: B <= 64.  The grid is 8 * ceil(B*H / 8) * nqb;
-// a workgroup past its XCD's items returns false.
-__device__ __forceinline__ bool balanced_jagged_item(const TileArgs& a, int nqb, int& b, int& h, int& qb) {
+// XCD's workgroups take its existing query blocks in a dense list, heaviest
+// first, and the workgroups past the list (the grid covers every pair at the
+// longest length) return false at the end of it.  The hardware starts the
+// workgroups in block order, each on its XCD, waiting while that XCD is full:
+// with the blocks past a short sequence's end spread through the order, the
+// XCDs holding the long sequences filled up early and held back the others
+// (2.5 workgroups per CU resident on the jagged workload, against 4 for
+// equal lengths).  One lane per sequence ranks the lengths (B <= 64) and one
+// lane per pair of the XCD counts its blocks (B*H <= 512).  Also returns the
+// sequence's first row and length.
+__device__ __forceinline__ bool balanced_jagged_item(const TileArgs& a, int& b, int& h, int& qb, int& s0b, int& lenb) {
   const int lane = threadIdx.x & 63;
   int len = -1;  // lanes past the batch rank after every sequence
+  int s0 = 0;
   if (lane < a.B) {
-    int s0, s1;
+    int s1;
     jagged_rows(a, lane, s0, s1);
     len = min(s1 - s0, a.N);
   }
@@ -537,20 +544,41 @@ __device__ __forceinline__ bool balanced_jagged_item(const TileArgs& a, int nqb,
     const int lt = __builtin_amdgcn_readlane(len, t);
     rank += (lt > len || (lt == len && t < lane)) ? 1 : 0;
   }
+  // lane r: length of the sequence of rank r
+  const int len_by_rank = __builtin_amdgcn_ds_permute(4 * (lane < a.B ? rank : lane), len);
   const int npairs = a.B * a.H;
-  const int x = blockIdx.x & 7, u = blockIdx.x >> 3;
-  // sorted pair i = 8 r + (r even ? x : 7 - x) belongs to XCD x; rows r < full
-  // are complete, row `full` holds the pairs below npairs
-  const int full = npairs >> 3, rem = npairs & 7;
-  const int n_x = full + ((((full & 1) ? 7 - x : x) < rem) ? 1 : 0);
-  if (n_x == 0) return false;
-  const int blk = u / n_x, j = u - blk * n_x;
-  if (blk >= nqb) return false;
-  const int i = 8 * j + ((j & 1) ? 7 - x : x);
-  const int srank = i / a.H;
-  h = i - srank * a.H;
-  b = __builtin_ctzll(__ballot(lane < a.B && rank == srank));
-  qb = nqb - 1 - blk;
+  const int x = blockIdx.x & 7;
+  const int u = blockIdx.x >> 3;
+  // lane k: this XCD's pair k, sorted pair i = 8 k + (k even ? x : 7 - x),
+  // with nb_k = ceil(L / 64) query blocks (non-increasing in k).  The XCD's
+  // items are listed densely, heaviest first: query block qb descending, then
+  // pair k, only blocks that exist (blocks nb_{k+1} .. nb_k - 1 exist for
+  // pairs 0 .. k); workgroups past the list have no item.
+  // (the shuffles run in every lane: a lane reads only active lanes)
+  const int ik = 8 * lane + ((lane & 1) ? 7 - x : x);
+  const int lk = __shfl(len_by_rank, min(ik / a.H, 63));
+  const int nb = ik < npairs ? (lk + 63) >> 6 : 0;
+  const int nb_up = __shfl(nb, (lane + 1) & 63);
+  const int nbn = lane < 63 ? nb_up : 0;
+  const int cnt = (nb - nbn) * (lane + 1);
+  int pre = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(pre, o);
+    if (lane >= o) pre += t;
+  }
+  const unsigned long long found = __ballot(pre > u);
+  if (found == 0) return false;
+  const int k = __builtin_ctzll(found);
+  const int v = u - __builtin_amdgcn_readlane(pre - cnt, k);
+  const int q = v / (k + 1), j = v - q * (k + 1);
+  qb = __builtin_amdgcn_readlane(nb, k) - 1 - q;
+  const int ij = 8 * j + ((j & 1) ? 7 - x : x);
+  const int sr = ij / a.H;
+  h = ij - sr * a.H;
+  b = __builtin_ctzll(__ballot(lane < a.B && rank == sr));
+  s0b = __builtin_amdgcn_readlane(s0, b);
+  lenb = __builtin_amdgcn_readlane(len, b);
   return true;
 }
 
@@ -573,19 +601,19 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
 
-  int b, h, qb;
+  int b, h, qb, s0, len;
   if (balanced) {
-    if (!balanced_jagged_item(a, nqb, b, h, qb)) return;  // uniform over the workgroup
+    if (!balanced_jagged_item(a, b, h, qb, s0, len)) return;  // uniform over the workgroup
   } else {
     int slot, bh;
     grouped_item(a.B * a.H, nqb, 4, bh, slot);
     h = bh % a.H;
     b = bh / a.H;
     qb = nqb - 1 - slot;  // heaviest blocks first
+    int s1;
+    jagged_rows(a, b, s0, s1);
+    len = min(s1 - s0, a.N);
   }
-  int s0, s1;
-  jagged_rows(a, b, s0, s1);
-  const int len = min(s1 - s0, a.N);
   const int q0 = qb * BMW;
   if (q0 >= len) return;  // uniform over the workgroup
   const long rs = (long)a.H * D;           // elements between consecutive rows
@@ -601,18 +629,6 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
   const int q0w = q0 + 32 * rg;
   const bool wave_live = q0w < len;
   const int qrow = q0w + n32;
-
-  // Q fragments, scaled by alpha log2(e) as in the tile kernel
-  bf16x8 qf[NDC];
-  const float beta = a.c * kLog2e;
-#pragma unroll
-  for (int c = 0; c < NDC; ++c) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (qrow < len) t = ldg16(qp + (long)qrow * rs + 16 * c + 8 * g2);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
-    qf[c] = as_bf16x8(t);
-  }
 
   // step t loads tiles 2t and 2t+1 straight into LDS: wave instruction w
   // fills bytes w KB .. +1 KB of each tensor's tile (the chunk swizzles applied
@@ -657,7 +673,19 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
-  dma_step(0, 0);
+  dma_step(0, 0);  // in flight while the Q fragments load
+  // Q fragments, scaled by alpha log2(e) as in the tile kernel
+  bf16x8 qf[NDC];
+  const float beta = a.c * kLog2e;
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+    if (qrow < len) t = ldg16(qp + (long)qrow * rs + 16 * c + 8 * g2);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) t[x] = pack_bf16x2(bf16_lo(t[x]) * beta, bf16_hi(t[x]) * beta);
+    qf[c] = as_bf16x8(t);
+  }
+
   wait_vmem();
   __syncthreads();
   for (int t = 0; t < steps; ++t) {
@@ -747,10 +775,10 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 template <bool CAUSAL>
 hipError_t launch_hstu_split(const TileArgs& a, hipStream_t stream) {
   const int nqb = (a.N + 63) / 64;
-  // XCD-balanced order when one wave can rank the sequences and there are
-  // enough (sequence, head) pairs for every XCD
+  // XCD-balanced order when one wave can rank the sequences and count one XCD's
+  // pairs, and there are enough (sequence, head) pairs for every XCD
   const long npairs = (long)a.H * a.B;
-  const int balanced = (a.B <= 64 && npairs >= 8) ? 1 : 0;
+  const int balanced = (a.B <= 64 && npairs >= 8 && npairs <= 512) ? 1 : 0;
   const long grid = balanced ? 8L * ((npairs + 7) / 8) * nqb : (long)nqb * npairs;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
