@@ -76,16 +76,17 @@ struct Cfg;
 // more were slower.
 //
 // kKAhead / kVAhead: LDS operand reads kept in flight ahead of the products
-// (K fragments of the score product, V^T fragments of the PV product), as many
-// as the register budget leaves room for; 0 leaves the order to the compiler
-// (measured faster for d = 64, whose four waves per SIMD hide the latency).
+// (K fragments of the score product, V^T fragments of the PV product); 0
+// leaves the order to the compiler (measured faster for d = 64, whose four
+// waves per SIMD hide the latency).  For d = 128, 3 and 2 measured ~1 %
+// faster than 3 and 3, 2 and 2, or 4 and 4.
 template <>
 struct Cfg<128> {
   static constexpr int BN = 32;
   static constexpr int kWavesPerSimd = 3;
   static constexpr int kHeadGroup = 4;
   static constexpr int kKAhead = 3;
-  static constexpr int kVAhead = 3;
+  static constexpr int kVAhead = 2;
 };
 template <>
 struct Cfg<256> {
