@@ -77,9 +77,10 @@ struct Cfg;
 //
 // kKAhead / kVAhead: LDS operand reads kept in flight ahead of the products
 // (K fragments of the score product, V^T fragments of the PV product); 0
-// leaves the order to the compiler (measured faster for d = 64, whose four
-// waves per SIMD hide the latency).  For d = 128, 3 and 2 measured ~1 %
-// faster than 3 and 3, 2 and 2, or 4 and 4.
+// leaves the order to the compiler.  With the three-level wave priorities of
+// the tile loop, 3 and 2 measured ~1 % faster than 3 and 3, 2 and 2 or 4 and 4
+// for d = 128, and ~1.5 % faster than the compiler's order for d = 64; d = 256
+// (one wave per SIMD) is fastest with 3 and 3.
 template <>
 struct Cfg<128> {
   static constexpr int BN = 32;
@@ -104,8 +105,8 @@ struct Cfg<64> {
   static constexpr int BN = 64;
   static constexpr int kWavesPerSimd = 4;
   static constexpr int kHeadGroup = 2;
-  static constexpr int kKAhead = 0;
-  static constexpr int kVAhead = 0;
+  static constexpr int kKAhead = 3;
+  static constexpr int kVAhead = 2;
 };
 
 // Layout of one K/V stage filled by direct HBM->LDS loads (1 KB of
