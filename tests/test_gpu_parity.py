@@ -423,16 +423,38 @@ def test_hstu_small_every_element(d, causal):
         assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
 
 
-@pytest.mark.parametrize("B,H", [(70, 1), (1, 4), (65, 2)])
+@pytest.mark.parametrize("B,H", [(70, 1), (1, 4), (65, 2), (64, 9)])
 def test_hstu_d64_unbalanced_dispatch(B, H):
     """The d = 64 kernel deals (sequence, head) pairs to the XCDs by length
-    only for 8 <= B*H and B <= 64 (a wave ranks the sequences); more than 64
-    sequences or fewer than eight pairs take the plain pair-major mapping."""
+    only for 8 <= B*H <= 512 and B <= 64 (a wave ranks the sequences and one
+    lane per pair of an XCD counts its blocks); more than 64 sequences, fewer
+    than eight pairs or more than 512 take the plain pair-major mapping."""
     _need_gpu()
     rng = np.random.default_rng(B * 10 + H)
     lengths = [int(v) for v in rng.integers(0, 200, B)]
     lengths[B // 2] = 257
     c = W.Jagged("hstu_unbalanced", B, H, 64, 1, 257, 0.3, 1.0 / 64, True, 45, 1.0)
+    x = W.jagged_inputs(c, lengths=lengths)
+    o = run_hstu(x, 1)
+    ref = hstu_ref(x, True)
+    for b, r in ref.items():
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        assert_bf16(o[s:e], r, f"seq {b} len {e - s}")
+
+
+@pytest.mark.parametrize("B,H,zeros", [(64, 8, 9), (16, 32, 3), (9, 1, 8)])
+def test_hstu_d64_balanced_dispatch_limits(B, H, zeros):
+    """The balanced d = 64 mapping at its limits: 512 pairs (64 per XCD, one
+    per lane of the list lookup) with 64 or 16 sequences, and 8 pairs with all
+    sequences but one empty (every other workgroup finds no item)."""
+    _need_gpu()
+    rng = np.random.default_rng(B * 1000 + H)
+    lengths = [int(v) for v in rng.integers(1, 160, B)]
+    for i in rng.choice(B, size=zeros, replace=False):
+        lengths[int(i)] = 0
+    if max(lengths) == 0:
+        lengths[0] = 97
+    c = W.Jagged("hstu_balanced_limits", B, H, 64, 1, max(lengths), 0.3, 1.0 / 64, True, 46, 1.0)
     x = W.jagged_inputs(c, lengths=lengths)
     o = run_hstu(x, 1)
     ref = hstu_ref(x, True)
