@@ -17,7 +17,9 @@ is already resident in HBM:
 ledger page (2 n^2 d per (b, h) for causal), from HIP events around every
 prefill launch on the stream the kernel runs on; decode GB/s, HSTU TFLOP/s and
 backward TFLOP/s (five products, 5 n^2 d per (b, h) causal) are reported
-beside it.  Prints ONE JSON line.
+beside it.  After the timed step, ``roofline.clock`` records the shader clock
+and socket power (amd-smi) while the prefill runs and the prefill's fraction
+of the peak recomputed at that clock.  Prints ONE JSON line.
 
 Other modes (used for profiling, see profiles/):
   --only prefill|decode|hstu|backward|decode_paged|hstu_padded|prefill_fp8   run just that part of the step
@@ -386,6 +388,65 @@ def _time_calls(fn, stream, warmup: int = 3, reps: int = 10) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def _smi_sample(exe: str):
+    """One `amd-smi metric` reading of GPU 0: (per-XCD shader clocks in MHz, socket power in W)."""
+    import subprocess
+
+    r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True, text=True,
+                       timeout=60)
+    text = r.stdout
+    start = min(i for i in (text.find("{"), text.find("[")) if i >= 0)
+    d = json.loads(text[start:])
+    g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+    clocks = []
+    for key in sorted(k for k in g["clock"] if k.startswith("gfx_")):
+        v = g["clock"][key]["clk"]["value"]
+        if isinstance(v, (int, float)):
+            clocks.append(float(v))
+    power = g["power"]["socket_power"]["value"]
+    return clocks, (float(power) if isinstance(power, (int, float)) else None)
+
+
+def clock_under_load(launch, samples: int = 2) -> dict:
+    """Shader clock and socket power while the headline prefill runs: a thread keeps
+    launching it while `amd-smi` (a child process) reads the GPU, then the
+    launches stop and the stream drains."""
+    import shutil
+    import threading
+
+    import torch
+
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    stop = threading.Event()
+
+    def keep_busy():
+        while not stop.is_set():
+            for _ in range(50):
+                launch()
+            torch.cuda.current_stream().synchronize()
+
+    t = threading.Thread(target=keep_busy, daemon=True)
+    t.start()
+    time.sleep(0.5)
+    got = []
+    err = None
+    for _ in range(samples):
+        try:
+            got.append(_smi_sample(exe))
+        except Exception as e:  # a missing or unparsable tool leaves the fields empty
+            err = f"{type(e).__name__}: {e}"
+    stop.set()
+    t.join()
+    torch.cuda.synchronize()
+    clocks = sorted(c for cl, _ in got for c in cl)
+    powers = [p for _, p in got if p is not None]
+    if not clocks:
+        return {"sclk_mhz": None, "socket_power_w": None, "note": err or "no clock reading"}
+    return {"sclk_mhz": clocks[len(clocks) // 2], "sclk_mhz_range": [clocks[0], clocks[-1]],
+            "socket_power_w": max(powers) if powers else None, "samples": len(got),
+            "source": "amd-smi metric while the prefill ran (median over XCDs and samples)"}
+
+
 def context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl, do, dlse):
     """Other prefill shapes and a decode split sweep, each timed with HIP events
     after the timed step."""
@@ -708,6 +769,14 @@ def main(argv=None) -> int:
             out["hstu_padded"]["jagged_speedup"] = round(ms["hstu_padded"] / ms["hstu"], 3)
         if out["value"] is None:
             out.update({"value": round(ms["hstu_padded"], 4), "unit": "ms", "higher_is_better": False})
+    if not args.only and not args.no_context and "prefill" in parts:
+        print("bench: shader clock and power under the prefill", file=sys.stderr, flush=True)
+        clk = clock_under_load(calls["prefill"])
+        if clk.get("sclk_mhz"):
+            peak_at = PEAK_BF16_TFLOPS * clk["sclk_mhz"] / (SPEC_CLOCK_HZ / 1e6)
+            clk["peak_at_sclk"] = round(peak_at, 1)
+            clk["frac_at_sclk"] = round(out["roofline"]["achieved"] / peak_at, 4)
+        out["roofline"]["clock"] = clk
     if not args.only and not args.no_context:
         print("bench: context measurements", file=sys.stderr, flush=True)
         out["context"] = context_measurements(fa, W, bf16, dev, stream, q, k, v, o, lse, pc, dx, dc, dq, dk, dv, dsl,
