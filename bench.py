@@ -393,7 +393,7 @@ def _smi_sample(exe: str):
     import subprocess
 
     r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True, text=True,
-                       timeout=60)
+                       timeout=20)
     text = r.stdout
     start = min(i for i in (text.find("{"), text.find("[")) if i >= 0)
     d = json.loads(text[start:])
