@@ -81,6 +81,18 @@ struct Cfg;
 // the tile loop, 3 and 2 measured ~1 % faster than 3 and 3, 2 and 2 or 4 and 4
 // for d = 128, and ~1.5 % faster than the compiler's order for d = 64; d = 256
 // (one wave per SIMD) is fastest with 3 and 3.
+// Per-lane LDS offsets of a tile kernel's operand reads; empty where the
+// kernel computes its addresses in the loop.
+template <bool ON, int NK, int NV>
+struct LaneOffsets {
+  uint32_t ka[NK], va[NV];
+};
+template <int NK, int NV>
+struct LaneOffsets<false, NK, NV> {
+  uint32_t* ka = nullptr;
+  uint32_t* va = nullptr;
+};
+
 template <>
 struct Cfg<128> {
   static constexpr int BN = 32;
@@ -88,6 +100,7 @@ struct Cfg<128> {
   static constexpr int kHeadGroup = 4;
   static constexpr int kKAhead = 3;
   static constexpr int kVAhead = 2;
+  static constexpr bool kStagePairs = true;
 };
 template <>
 struct Cfg<256> {
@@ -99,6 +112,7 @@ struct Cfg<256> {
   static constexpr int kHeadGroup = 4;
   static constexpr int kKAhead = 3;
   static constexpr int kVAhead = 3;
+  static constexpr bool kStagePairs = true;
 };
 template <>
 struct Cfg<64> {
@@ -107,6 +121,7 @@ struct Cfg<64> {
   static constexpr int kHeadGroup = 2;
   static constexpr int kKAhead = 3;
   static constexpr int kVAhead = 2;
+  static constexpr bool kStagePairs = false;
 };
 
 // Layout of one K/V stage filled by direct HBM->LDS loads (1 KB of
@@ -264,6 +279,32 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
     const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int tr_byte = 8 * (lane & 1);
 
+    // Per-lane LDS byte offsets of the operand reads within a stage.  The
+    // swizzles depend only on the low row bits a lane fixes (kswz on bits
+    // 0..3 of the key row, vswz on bits 0..1 of the V row), so the 32-key
+    // block, the 16-row half and the upper 4 rows of a transposing read are
+    // immediate offsets: K fragment (c, kb) is at ka[c] + 32 kb kRow, V^T
+    // fragment (kb, jj, db) at va[db] + (32 kb + 16 jj) vRow.  The empty asm
+    // keeps each offset in a register of its own, so the tile loop adds
+    // nothing per read.
+    LaneOffsets<Cfg<D>::kStagePairs, NDC, NDB> lo;
+    uint32_t* const ka = lo.ka;
+    uint32_t* const va = lo.va;
+    if constexpr (Cfg<D>::kStagePairs) {
+      const int kr0 = key_perm(n32);
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) {
+        ka[c] = (uint32_t)(kr0 * L::kRow + (((2 * c + g2) ^ L::kswz(kr0)) << 4));
+        asm volatile("" : "+v"(ka[c]));
+      }
+      const int vr0 = 8 * g2 + tr_row;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        va[db] = (uint32_t)(vr0 * L::vRow + (((4 * db + tr_chunk) ^ L::vswz(vr0)) << 4) + tr_byte);
+        asm volatile("" : "+v"(va[db]));
+      }
+    }
+
     // ---- accumulators and running statistics
     f32x16 acc[NDB];
 #pragma unroll
@@ -278,8 +319,17 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
     wait_vmem();
     __syncthreads();
 
-    for (int j = 0; j < n_tiles; ++j) {
-      const int buf = j & 1;
+    // Tiles go two at a time where the stage pairs are on: the inner loop is
+    // unrolled, so the LDS stage is a compile-time constant and every LDS
+    // read of a tile is one per-lane address register plus an immediate
+    // offset, with no address arithmetic per read.
+    constexpr int SU = Cfg<D>::kStagePairs ? 2 : 1;
+    for (int j0 = 0; j0 < n_tiles; j0 += SU)
+#pragma unroll
+    for (int su = 0; su < SU; ++su) {
+      const int j = j0 + su;
+      if (SU > 1 && j >= n_tiles) break;  // uniform over the workgroup
+      const int buf = SU > 1 ? su : (j & 1);
       const int k0 = j * BN;
       const bool has_next = j + 1 < n_tiles;
       // the other buffer's tile was last read before the previous barrier
@@ -297,6 +347,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
         // S^T = K Q^T
         f32x16 s[NKB];
         auto kread = [&](int c, int kb) {
+          if constexpr (Cfg<D>::kStagePairs) return *reinterpret_cast<const u32x4*>(sk + 32 * kb * L::kRow + ka[c]);
           const int kr_ = 32 * kb + key_perm(n32);
           return *reinterpret_cast<const u32x4*>(sk + kr_ * L::kRow + (((2 * c + g2) ^ L::kswz(kr_)) << 4));
         };
@@ -409,7 +460,9 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::kWavesPerSimd) void tile_kernel(T
         // O^T += V^T P^T; V^T fragments gathered by transposing reads
         auto vread = [&](int kb, int jj, int db) {
           const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
-          const unsigned char* addr = sv + krow * L::vRow + (((4 * db + tr_chunk) ^ L::vswz(krow)) << 4) + tr_byte;
+          const unsigned char* addr =
+              Cfg<D>::kStagePairs ? sv + (32 * kb + 16 * jj) * L::vRow + va[db]
+                                  : sv + krow * L::vRow + (((4 * db + tr_chunk) ^ L::vswz(krow)) << 4) + tr_byte;
           const u32x2 lo = lds_read_tr16(addr);
           const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
           return u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -694,8 +747,34 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 
   wait_vmem();
   __syncthreads();
-  for (int t = 0; t < steps; ++t) {
-    const int buf = t & 1;
+  // Per-lane LDS byte offsets of the operand reads (this wave's key half
+  // included); the swizzles depend only on low row bits the lane fixes, so
+  // the 16-row half and the upper 4 rows of a transposing read are immediate
+  // offsets, and with the stage a compile-time constant (steps taken two at
+  // a time) the step adds nothing per read.
+  uint32_t ka[NDC], va[NDB];
+  {
+    const int kr0 = key_perm(n32);
+    const int vr0 = 8 * g2 + tr_row;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      ka[c] = (uint32_t)(ks * 2 * L::stage + kr0 * L::kRow + (((2 * c + g2) ^ L::kswz(kr0)) << 4));
+      asm volatile("" : "+v"(ka[c]));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      va[db] = (uint32_t)(ks * 2 * L::stage + L::kBytes + vr0 * L::vRow +
+                          (((4 * db + tr_chunk) ^ L::vswz(vr0)) << 4) + tr_byte);
+      asm volatile("" : "+v"(va[db]));
+    }
+  }
+
+  for (int t0 = 0; t0 < steps; t0 += 2)
+#pragma unroll
+  for (int su = 0; su < 2; ++su) {
+    const int t = t0 + su;
+    if (t >= steps) break;  // uniform over the workgroup
+    const int buf = su;
     const bool has_next = t + 1 < steps;
     // the other buffers' tiles were last read before the previous barrier
     if (has_next) dma_step(t + 1, buf ^ 1);
@@ -703,14 +782,12 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
     const int k0 = ti * BN;
     const bool active = wave_live && ti < n_tiles && !(CAUSAL && k0 > q0w + 31);
     if (active) {
-      const unsigned char* sk = smem + (ks * 2 + buf) * L::stage;
-      const unsigned char* sv = sk + L::kBytes;
+      const unsigned char* sb = smem + buf * L::stage;
       __builtin_amdgcn_s_setprio(1);
       f32x16 s;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
-        const int kr_ = key_perm(n32);
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + kr_ * L::kRow + (((2 * c + g2) ^ L::kswz(kr_)) << 4));
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(sb + ka[c]);
         const f32x16 zero = {};
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), qf[c], c == 0 ? zero : s, 0, 0, 0);
       }
@@ -733,12 +810,9 @@ __global__ __launch_bounds__(kThreads, 4) void hstu_split_kernel(TileArgs a, int
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const u32x4 pw = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
-        const int krow = 16 * jj + 8 * g2 + tr_row;
-        const unsigned char* vrow = sv + krow * L::vRow;
-        const int swz = L::vswz(krow);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const unsigned char* addr = vrow + (((4 * db + tr_chunk) ^ swz) << 4) + tr_byte;
+          const unsigned char* addr = sb + 16 * jj * L::vRow + va[db];
           const u32x2 lo = lds_read_tr16(addr);
           const u32x2 hi = lds_read_tr16(addr + 4 * L::vRow);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
