@@ -176,15 +176,45 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
+  // Per-lane LDS byte offsets of the operand reads within a stage.  The
+  // swizzle depends only on bits 0..3 of the row, which the lane fixes, so
+  // the 32-key block, the 16-row half and K against V are immediate offsets:
+  // K (V) fragment (c, kb) at op_off[c] + 32 kb ROW (+ TILE), the two halves
+  // of K^T piece (kb, jj, db) at tlo_off[db] / thi_off[db] + (32 kb + 16 jj)
+  // ROW.  With the stage a compile-time constant (tiles two at a time, the
+  // inner loop unrolled) a tile adds nothing per read; the empty asm keeps
+  // each offset in a register of its own.
+  uint32_t op_off[NDC], tlo_off[NDB], thi_off[NDB];
+  {
+    const int r = key_perm(n32);
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      op_off[c] = (uint32_t)(r * ROW + (((2 * c + g2) ^ swz_kv<D>(r)) << 4));
+      asm volatile("" : "+v"(op_off[c]));
+    }
+    const int kr = 8 * g2 + tr_row;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int ch = 4 * db + tr_chunk;
+      tlo_off[db] = (uint32_t)(kr * ROW + ((ch ^ swz_kv<D>(kr)) << 4) + tr_byte);
+      thi_off[db] = (uint32_t)((kr + 4) * ROW + ((ch ^ swz_kv<D>(kr + 4)) << 4) + tr_byte);
+      asm volatile("" : "+v"(tlo_off[db]), "+v"(thi_off[db]));
+    }
+  }
+
   load_tile(0);
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j0 = 0; j0 < n_tiles; j0 += 2)
+#pragma unroll
+  for (int su = 0; su < 2; ++su) {
+    const int j = j0 + su;
+    if (j >= n_tiles) break;  // uniform over the workgroup
     wait_vmem();      // this wave's pieces of tile j have landed
     __syncthreads();  // everyone's have; stage (j+1)&1 is free
     if (j + 1 < n_tiles) load_tile(j + 1);
     const int k0 = j * kBN;
     const bool active = wave_live && !(CAUSAL && k0 > q0w + 31);
     if (!active) continue;
-    const unsigned char* sk = smem + (j & 1) * 2 * TILE;
+    const unsigned char* sk = smem + su * 2 * TILE;
     const unsigned char* sv = sk + TILE;
 
     __builtin_amdgcn_s_setprio(1);  // products first: other waves fill the gaps with elementwise work
@@ -194,8 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
     for (int c = 0; c < NDC; ++c) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int r = 32 * kb + key_perm(n32);
-        const int off = r * ROW + (((2 * c + g2) ^ swz_kv<D>(r)) << 4);
+        const uint32_t off = 32 * kb * ROW + op_off[c];
         const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + off);
         const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + off);
         const f32x16 zero = {};
@@ -233,12 +262,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int nq) 
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
-        const int krow = 32 * kb + 16 * jj + 8 * g2 + tr_row;
+        const unsigned char* sb = sk + (32 * kb + 16 * jj) * ROW;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int ch = 4 * db + tr_chunk;
-          const u32x2 lo = lds_read_tr16(sk + krow * ROW + ((ch ^ swz_kv<D>(krow)) << 4) + tr_byte);
-          const u32x2 hi = lds_read_tr16(sk + (krow + 4) * ROW + ((ch ^ swz_kv<D>(krow + 4)) << 4) + tr_byte);
+          const u32x2 lo = lds_read_tr16(sb + tlo_off[db]);
+          const u32x2 hi = lds_read_tr16(sb + thi_off[db]);
           const u32x4 kt = {lo[0], lo[1], hi[0], hi[1]};
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt), as_bf16x8(pw), acc[db], 0, 0, 0);
         }

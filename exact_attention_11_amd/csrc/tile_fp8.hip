@@ -162,8 +162,35 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  // Per-lane LDS byte offsets of the operand reads within a stage.  The
+  // swizzles depend only on row bits the lane fixes (bits 1..3 of the key
+  // row, bits 1..2 of the V row), so the 32-key block and the 8-row step of a
+  // transposing read are immediate offsets: K fragment halves (c, kb) at
+  // klo_off[c] / khi_off[c] + 32 kb ROW, V^T piece (db, u) at
+  // v_off[db] + 8 u ROW + TILE.  With the stage a compile-time constant
+  // (tiles two at a time, the inner loop unrolled) a tile adds nothing per
+  // read; the empty asm keeps each offset in a register of its own.
+  uint32_t klo_off[NKC], khi_off[NKC], v_off[NDB];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    const int ch = 4 * c + 2 * g2;
+    klo_off[c] = (uint32_t)(n32 * ROW + ((ch ^ swz_k(n32)) << 4));
+    khi_off[c] = (uint32_t)(n32 * ROW + (((ch + 1) ^ swz_k(n32)) << 4));
+    asm volatile("" : "+v"(klo_off[c]), "+v"(khi_off[c]));
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int ch = 2 * db + (g4 & 1);
+    v_off[db] = (uint32_t)(tr_row0 * ROW + ((ch ^ swz_v(tr_row0)) << 4) + tr_byte);
+    asm volatile("" : "+v"(v_off[db]));
+  }
+
+  for (int j0 = 0; j0 < n_tiles; j0 += 2)
+#pragma unroll
+  for (int su = 0; su < 2; ++su) {
+    const int j = j0 + su;
+    if (j >= n_tiles) break;  // uniform over the workgroup
+    const int buf = su;
     const int k0 = j * kBN;
     const bool has_next = j + 1 < n_tiles;
     // the other buffer's tile was last read before the previous barrier
@@ -184,10 +211,8 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
       u32x4 klo[ST], khi[ST];
       auto kread = [&](int t) {
         const int kb = t % 2, c = t / 2;
-        const int r = 32 * kb + n32;
-        const int ch = 4 * c + 2 * g2;
-        klo[t] = *reinterpret_cast<const u32x4*>(sk + r * ROW + ((ch ^ swz_k(r)) << 4));
-        khi[t] = *reinterpret_cast<const u32x4*>(sk + r * ROW + (((ch + 1) ^ swz_k(r)) << 4));
+        klo[t] = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROW + klo_off[c]);
+        khi[t] = *reinterpret_cast<const u32x4*>(sk + 32 * kb * ROW + khi_off[c]);
       };
 #pragma unroll
       for (int t = 0; t < KW; ++t) kread(t);
@@ -255,13 +280,10 @@ __global__ __launch_bounds__(kThreads, 3) void tile_fp8_kernel(Fp8Args a, int nq
       // O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int ch = 2 * db + (g4 & 1);
         i32x8 vt;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int r = tr_row0 + 8 * u;
-          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)(sv + r * ROW + ((ch ^ swz_v(r)) << 4) + tr_byte));
+          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sv + 8 * u * ROW + v_off[db]));
           vt[2 * u] = x[0];
           vt[2 * u + 1] = x[1];
         }
