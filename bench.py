@@ -58,6 +58,10 @@ SPEC_CLOCK_HZ = 2.4e9
 # SIMD, measured with an in-bounds microbenchmark (v_rcp_f32 taken at the
 # same rate): the HSTU weight needs two per score.
 TRANS_CYCLES_PER_WAVE_OP = 8.5
+# Issue cycles of one 64-lane plain f32 VALU instruction on one SIMD (16 lanes
+# per cycle); the SiLU weight adds an add, a multiply and half a bf16 pack per
+# score to its two transcendentals.
+VALU_CYCLES_PER_WAVE_OP = 4.0
 TILE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/tile_bf16.hip", "exact_attention_11_amd/csrc/common.hpp",
                        "exact_attention_11_amd/csrc/launch.hpp"]
 DECODE_KERNEL_SOURCES = ["exact_attention_11_amd/csrc/decode.hip", "exact_attention_11_amd/csrc/common.hpp",
@@ -733,10 +737,15 @@ def main(argv=None) -> int:
         # scores counted by the same causal convention (flops / 4d)
         scores = hf / (4 * jc.d)
         trans_ms = 2 * scores / 64 * TRANS_CYCLES_PER_WAVE_OP / (SIMDS * SPEC_CLOCK_HZ) * 1e3
+        # vector-issue bound of the whole weight: the transcendentals plus the
+        # plain instructions each score needs
+        silu_ms = trans_ms + 2.5 * scores / 64 * VALU_CYCLES_PER_WAVE_OP / (SIMDS * SPEC_CLOCK_HZ) * 1e3
         out["hstu"] = {"TFLOP/s": round(ht, 2), "frac_bf16_peak": round(ht / PEAK_BF16_TFLOPS, 4),
                        "ms_per_call": round(ms["hstu"], 4), "median_ms_per_call": round(med["hstu"], 4),
                        "flops": hf, "trans_bound_ms": round(trans_ms, 4),
-                       "frac_trans_bound": round(trans_ms / ms["hstu"], 4)}
+                       "frac_trans_bound": round(trans_ms / ms["hstu"], 4),
+                       "silu_valu_bound_ms": round(silu_ms, 4),
+                       "frac_silu_valu_bound": round(silu_ms / ms["hstu"], 4)}
         if out["value"] is None:
             out.update({"value": round(ht, 2), "unit": "TFLOP/s"})
     if "backward" in parts:
